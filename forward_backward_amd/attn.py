@@ -1,0 +1,173 @@
+"""Python binding of libattn.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI of
+``include/attn.h``; this module only checks tensor metadata, allocates
+outputs and workspaces through torch, and passes raw device pointers and the
+current HIP stream. There is no fallback: without the built library every
+call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_BF16, ATTN_FP32 = 0, 1
+OP_FWD, OP_BWD, OP_DECODE = 0, 1, 2
+
+_DTYPES = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_FP32}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn status {status}: {message}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32),
+        ("Tq", ctypes.c_int32),
+        ("Tkv", ctypes.c_int32),
+        ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("kv_lens", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+_P = ctypes.POINTER(Params)
+_V = ctypes.c_void_p
+_SIGS = {
+    "attn_validate": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "attn_fwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
+    "attn_bwd_workspace_size": (ctypes.c_size_t, [_P]),
+    "attn_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "attn_decode_num_splits": (ctypes.c_int32, [_P]),
+    "attn_decode_workspace_size": (ctypes.c_size_t, [_P, ctypes.c_int32]),
+    "attn_decode": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_int32, _V, ctypes.c_size_t, _V]),
+    "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_last_error": (ctypes.c_char_p, []),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def lib(path: str = LIB_PATH):
+    """Load libattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m forward_backward_amd.build`")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        L = lib()
+        raise AttnError(status, f"{L.attn_status_string(status).decode()}: {L.attn_last_error().decode()}")
+
+
+def make_params(B, Tq, Tkv, Hq, Hkv, D, dtype=ATTN_BF16, scale=None, causal=False, kv_lens_ptr=None) -> Params:
+    return Params(B, Tq, Tkv, Hq, Hkv, D, dtype, float(1.0 / math.sqrt(D) if scale is None else scale),
+                  int(bool(causal)), kv_lens_ptr)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _tensor4(name, t):
+    if not isinstance(t, torch.Tensor) or t.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D tensor [B, T, H, D]")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name} must be bfloat16 or float32")
+
+
+def _params_for(q, k, scale, causal, kv_lens):
+    _tensor4("q", q)
+    _tensor4("k", k)
+    if q.dtype != k.dtype:
+        raise ValueError("q and k must share a dtype")
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != q.shape[0]:
+            raise ValueError("kv_lens must be a device int32 tensor of length B")
+    B, Tq, Hq, D = q.shape
+    _, Tkv, Hkv, _ = k.shape
+    return make_params(B, Tq, Tkv, Hq, Hkv, D, _DTYPES[q.dtype], scale, causal,
+                       None if kv_lens is None else kv_lens.data_ptr())
+
+
+def fwd(q, k, v, scale=None, causal=False, kv_lens=None, out=None, lse=None):
+    """O [B,Tq,Hq,D] (dtype of q) and LSE fp32 [B,Hq,Tq] via attn_fwd."""
+    p = _params_for(q, k, scale, causal, kv_lens)
+    _tensor4("v", v)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k")
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((p.B, p.Hq, p.Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _stream()))
+    return o, lse_t
+
+
+def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_lens=None, workspace=None):
+    """dQ, dK, dV via attn_bwd (deterministic two-pass backward)."""
+    p = _params_for(q, k, scale, causal, kv_lens)
+    for name, t, ref in (("v", v, k), ("o", o, q), ("do", do, q)):
+        _tensor4(name, t)
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of {'k' if ref is k else 'q'}")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = lib().attn_bwd_workspace_size(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                          _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+    return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, kv_lens=None, scale=None, num_splits=0, want_lse=True):
+    """Split-KV decode: O [B,Tq,Hq,D] bf16 and LSE fp32 [B,Hq,Tq] (or None)."""
+    p = _params_for(q, k_cache, scale, False, kv_lens)
+    _tensor4("v_cache", v_cache)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    o = torch.empty_like(q)
+    lse_t = torch.empty((p.B, p.Hq, p.Tq), dtype=torch.float32, device=q.device) if want_lse else None
+    need = lib().attn_decode_workspace_size(ctypes.byref(p), num_splits)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse_t),
+                             num_splits, _ptr(ws), ws.numel(), _stream()))
+    return o, lse_t
+
+
+def decode_num_splits(B, Tq, Tkv, Hq, Hkv, D) -> int:
+    p = make_params(B, Tq, Tkv, Hq, Hkv, D)
+    return int(lib().attn_decode_num_splits(ctypes.byref(p)))

@@ -1,0 +1,193 @@
+// C ABI of the attention library: validation, workspace queries, launches.
+//
+// Validation runs on the host before any HIP call, so every argument error
+// is reported without touching a device (and can be exercised on a host
+// without a GPU). The library allocates nothing and never synchronises.
+#include "../../include/attn.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "attn_internal.h"
+
+namespace attn {
+void launch_delta_any(const BwdArgs& a, int D, bool bf16, hipStream_t s);
+}
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+attn_status_t fail(attn_status_t st, const char* fmt, int x = 0, int y = 0) {
+  std::snprintf(g_last_error, sizeof(g_last_error), fmt, x, y);
+  return st;
+}
+
+attn_status_t ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr long kMaxGrid = 2147483647L;
+constexpr float kLog2e = 1.4426950408889634f;
+
+int elem_bytes(const attn_params_t* p) { return p->dtype == ATTN_FP32 ? 4 : 2; }
+
+size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
+  if (p == nullptr) return fail(ATTN_ERR_INVALID, "params is NULL");
+  if (op != ATTN_OP_FWD && op != ATTN_OP_BWD && op != ATTN_OP_DECODE)
+    return fail(ATTN_ERR_INVALID, "unknown op %d", op);
+  if (p->B < 0 || p->Tq < 0 || p->Tkv < 0)
+    return fail(ATTN_ERR_INVALID, "B, Tq and Tkv must be >= 0");
+  if (p->Hq < 1 || p->Hkv < 1) return fail(ATTN_ERR_INVALID, "Hq and Hkv must be >= 1");
+  if (p->Hq % p->Hkv != 0) return fail(ATTN_ERR_INVALID, "Hq (%d) is not a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP32) return fail(ATTN_ERR_INVALID, "unknown dtype %d", p->dtype);
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID, "causal must be 0 or 1, got %d", p->causal);
+  if (!(std::isfinite(p->scale) && p->scale > 0.f)) return fail(ATTN_ERR_INVALID, "scale must be finite and > 0");
+  if (p->causal && p->Tq != p->Tkv)
+    return fail(ATTN_ERR_INVALID, "causal masking needs Tq == Tkv (got %d and %d)", p->Tq, p->Tkv);
+  if (op == ATTN_OP_DECODE && p->causal) return fail(ATTN_ERR_INVALID, "decode is non-causal");
+  if (p->D != 64 && p->D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", p->D);
+  if (op == ATTN_OP_DECODE && p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is bf16 only");
+  const long qrows = (long)p->B * p->Hq * p->Tq;
+  const long krows = (long)p->B * p->Hkv * p->Tkv;
+  if (qrows >= kMaxGrid || krows >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+  return ok();
+}
+
+size_t attn_bwd_workspace_size(const attn_params_t* p) {
+  if (p == nullptr) return 0;
+  return round_up((size_t)(p->B > 0 ? p->B : 0) * (p->Hq > 0 ? p->Hq : 0) * (p->Tq > 0 ? p->Tq : 0) * sizeof(float),
+                  256);
+}
+
+attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* stream) {
+  attn_status_t st = attn_validate(p, ATTN_OP_FWD);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  attn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.kv_lens = p->kv_lens;
+  a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
+  a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->dtype == ATTN_BF16) {
+    a.num_qtiles = (p->Tq + attn::kFwdBlockM - 1) / attn::kFwdBlockM;
+    if ((long)a.num_qtiles * a.Hq * a.B >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+    e = attn::launch_fwd_bf16(a, p->D, s);
+  } else {
+    a.num_qtiles = p->Tq;
+    e = attn::launch_fwd_fp32(a, p->D, s);
+  }
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
+  return ok();
+}
+
+attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  attn_status_t st = attn_validate(p, ATTN_OP_BWD);
+  if (st != ATTN_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const size_t need = attn_bwd_workspace_size(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%d bytes needed)", (int)need);
+  attn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = static_cast<float*>(workspace); a.kv_lens = p->kv_lens;
+  a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
+  a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
+  a.num_qtiles = (p->Tq + attn::kBwdBlockM - 1) / attn::kBwdBlockM;
+  a.num_ktiles = (p->Tkv + attn::kBwdBlockN - 1) / attn::kBwdBlockN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = p->dtype == ATTN_BF16 ? attn::launch_bwd_bf16(a, p->D, s) : attn::launch_bwd_fp32(a, p->D, s);
+  if (e == hipErrorNotSupported) return fail(ATTN_ERR_UNSUPPORTED, "no kernel for this configuration");
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
+  return ok();
+}
+
+int32_t attn_decode_num_splits(const attn_params_t* p) {
+  if (p == nullptr || p->Tkv <= 0) return 1;
+  // Fixed key range per split (a pure function of the shape): 512 keys, so
+  // that a batch's active splits scale with its KV length and every split
+  // streams the same amount of K/V.
+  const int split_len = 512;
+  int s = (p->Tkv + split_len - 1) / split_len;
+  return s < 1 ? 1 : s;
+}
+
+static int decode_split_len(const attn_params_t* p, int num_splits) {
+  const int t = attn::kDecodeTileN;
+  int per = (p->Tkv + num_splits - 1) / num_splits;
+  per = (per + t - 1) / t * t;
+  return per < t ? t : per;
+}
+
+size_t attn_decode_workspace_size(const attn_params_t* p, int32_t num_splits) {
+  if (p == nullptr || p->Hkv < 1 || p->Hq < p->Hkv) return 0;
+  if (num_splits <= 0) num_splits = attn_decode_num_splits(p);
+  const size_t rows = (size_t)(p->B > 0 ? p->B : 0) * p->Hkv * num_splits * (size_t)(p->Tq > 0 ? p->Tq : 0) *
+                      (p->Hq / p->Hkv);
+  const size_t o_bytes = round_up(rows * (size_t)p->D * sizeof(float), 256);
+  const size_t l_bytes = round_up(rows * sizeof(float), 256);
+  return o_bytes + l_bytes;
+}
+
+attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache, void* o,
+                          float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status_t st = attn_validate(p, ATTN_OP_DECODE);
+  if (st != ATTN_OK) return st;
+  if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  if (num_splits < 0) return fail(ATTN_ERR_INVALID, "num_splits must be >= 0 (0 = automatic)");
+  if (num_splits == 0) num_splits = attn_decode_num_splits(p);
+  const size_t need = attn_decode_workspace_size(p, num_splits);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%d bytes needed)", (int)need);
+  const long rows = (long)p->B * p->Hkv * num_splits;
+  if (rows >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "too many splits");
+  attn::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_lens = p->kv_lens;
+  const size_t prow = (size_t)p->B * p->Hkv * num_splits * (size_t)p->Tq * (p->Hq / p->Hkv);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(prow * p->D * sizeof(float), 256));
+  a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
+  a.scale = p->scale; a.scale_log2 = p->scale * kLog2e;
+  a.num_splits = num_splits;
+  a.split_len = decode_split_len(p, num_splits);
+  hipError_t e = attn::launch_decode_bf16(a, p->D, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return fail(ATTN_ERR_UNSUPPORTED, "no kernel for this configuration");
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
+  return ok();
+}
+
+const char* attn_status_string(attn_status_t status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

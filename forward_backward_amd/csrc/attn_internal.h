@@ -1,0 +1,76 @@
+// Internal host/device interface between the C ABI (attn_api.cpp) and the
+// HIP kernels. Not installed; callers use include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Arguments of the forward kernels (bf16 tiles or the fp32 path).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;              // [B, Hq, Tq], natural log
+  const int32_t* kv_lens;  // device [B] or nullptr
+  int B, Tq, Tkv, Hq, Hkv;
+  float scale;             // softmax scale
+  float scale_log2;        // scale * log2(e): the kernels work in base 2
+  int causal;
+  int num_qtiles;
+};
+
+// Arguments of the backward kernels.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;            // workspace: D = rowsum(dO * O), [B, Hq, Tq]
+  const int32_t* kv_lens;
+  int B, Tq, Tkv, Hq, Hkv;
+  float scale;
+  float scale_log2;
+  int causal;
+  int num_qtiles;          // query tiles of the dQ kernel
+  int num_ktiles;          // KV tiles of the dK/dV kernel
+};
+
+// Arguments of the split-KV decode kernels.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;              // optional [B, Hq, Tq]
+  float* part_o;           // workspace [B, Hkv, S, Tq*G, D] fp32
+  float* part_lse;         // workspace [B, Hkv, S, Tq*G] fp32 (natural log)
+  const int32_t* kv_lens;
+  int B, Tq, Tkv, Hq, Hkv;
+  float scale;
+  float scale_log2;
+  int num_splits;          // S
+  int split_len;           // keys per split (a multiple of the key tile)
+};
+
+// Launchers (each returns the hipGetLastError() after its launches).
+hipError_t launch_fwd_bf16(const FwdArgs& a, int D, hipStream_t s);
+hipError_t launch_fwd_fp32(const FwdArgs& a, int D, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int D, hipStream_t s);
+hipError_t launch_bwd_fp32(const BwdArgs& a, int D, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s);
+
+// Tile sizes the host needs for grids and workspaces.
+constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
+constexpr int kBwdBlockM = 64;    // query rows per dQ workgroup
+constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
+constexpr int kDecodeTileN = 64;  // keys per decode iteration
+
+}  // namespace attn

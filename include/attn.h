@@ -1,0 +1,127 @@
+/*
+ * attn.h - C ABI of the fused exact attention library for AMD MI355X (gfx950).
+ *
+ * Operation (probjax benchmark pages, "Attention performance", introduction
+ * and section "Memory"): for tensors laid out [batch, seq, heads, head_dim],
+ *     O = softmax(scale * Q K^T + mask) V,
+ * keeping O and the log-sum-exp of each row for the backward pass, and the
+ * gradients of a scalar loss with respect to Q, K and V given dO.
+ *
+ * Masks:
+ *   - causal, equal-length form: key j is visible to query i iff j <= i
+ *     ("Attention performance", section "When to use which");
+ *   - per-batch KV length (the pages' KVLenMask): keys j >= kv_lens[b] are
+ *     skipped; a query row with no valid key returns zeros
+ *     ("H100 (Hopper)", section "Mosaic GPU");
+ *   - grouped-query attention: query head h reads KV head h / (Hq / Hkv),
+ *     without repeating K or V ("Attention performance", section
+ *     "Grouped-query attention and decoding").
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *     in [B, T, H, D] order (row stride H*D elements) and 16-byte aligned.
+ *     Q, dO, O, dQ: [B, Tq, Hq, D]; K, V, dK, dV: [B, Tkv, Hkv, D].
+ *     Tensors are bf16 or fp32 as given by attn_params_t.dtype.
+ *   - LSE is fp32 [B, Hq, Tq], natural logarithm, -inf on rows with no
+ *     valid key (where O is 0).
+ *   - kv_lens, when not NULL, is a DEVICE int32 [B]; each value is clamped
+ *     to [0, Tkv] by the kernels (the host cannot read it without a sync).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
+ *     asynchronous on it. The library never allocates, frees or
+ *     synchronises, holds no state and is safe to call from several threads.
+ *   - Argument errors are reported before anything is launched: the call
+ *     returns a status and attn_last_error() (thread-local) describes it.
+ *     The pages' own rule is to reject what cannot be computed exactly
+ *     ("H100 (Hopper)", section "Device-specific defaults").
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* null pointer, bad sizes, Hq % Hkv != 0, causal with Tq != Tkv, bad scale */
+  ATTN_ERR_UNSUPPORTED = 2, /* head_dim or dtype this build has no kernel for */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size query */
+  ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+typedef enum { ATTN_OP_FWD = 0, ATTN_OP_BWD = 1, ATTN_OP_DECODE = 2 } attn_op_t;
+
+typedef struct {
+  int32_t B;      /* batch, >= 0 */
+  int32_t Tq;     /* query length, >= 0 */
+  int32_t Tkv;    /* key/value length (KV cache capacity for decode), >= 0 */
+  int32_t Hq;     /* query heads, >= 1 */
+  int32_t Hkv;    /* key/value heads, >= 1, divides Hq */
+  int32_t D;      /* head_dim: 64 or 128 */
+  int32_t dtype;  /* attn_dtype_t of Q, K, V, O, dO, dQ, dK, dV */
+  float scale;    /* softmax scale, finite and >= 0 (e.g. 1/sqrt(D)) */
+  int32_t causal; /* 0 or 1; 1 requires Tq == Tkv */
+  const int32_t* kv_lens; /* device int32[B] or NULL (= Tkv for every batch) */
+} attn_params_t;
+
+/* Host-only check of `p` for operation `op` (attn_op_t). Touches no device
+ * and no HIP runtime; returns ATTN_OK or the status the call would return. */
+attn_status_t attn_validate(const attn_params_t* p, int32_t op);
+
+/* Forward (online softmax over KV tiles).
+ * q [B,Tq,Hq,D], k/v [B,Tkv,Hkv,D] in; o [B,Tq,Hq,D], lse fp32 [B,Hq,Tq] out.
+ * Only KV tiles below min(Tkv, kv_lens[b]) and, with causal, below the
+ * query tile's last row are read. */
+attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o,
+                       float* lse, void* stream);
+
+/* Bytes of device workspace attn_bwd needs (fp32 D = rowsum(dO * O)). */
+size_t attn_bwd_workspace_size(const attn_params_t* p);
+
+/* Backward: deterministic two-pass scheme without atomics. A pre-kernel
+ * forms D = rowsum(dO * O) in the workspace; one kernel forms dK and dV per
+ * KV tile (summing the G query heads of a group in a fixed order); one
+ * kernel forms dQ per query tile. P is recomputed from `lse`.
+ * q, k, v, o, lse as produced/consumed by attn_fwd; dout = dO like q.
+ * dq like q; dk, dv like k. Keys at or past kv_lens[b] get dK = dV = 0.
+ * Reruns on the same inputs are bitwise identical. */
+attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Split count attn_decode uses when num_splits = 0 (a pure function of the
+ * shape, so reruns are bitwise identical). */
+int32_t attn_decode_num_splits(const attn_params_t* p);
+
+/* Bytes of device workspace attn_decode needs for `num_splits` (0 = auto):
+ * fp32 partial outputs and partial LSEs per split. */
+size_t attn_decode_workspace_size(const attn_params_t* p, int32_t num_splits);
+
+/* Split-KV decode ("Attention performance", section "Grouped-query attention
+ * and decoding"): few queries over a long KV cache. The keys are split
+ * across workgroups, the Tq queries of the G heads of a KV group are packed
+ * into one tile, and the partial results are combined by their LSE in a
+ * fixed split order. Non-causal (p->causal must be 0); bf16 only.
+ * q [B,Tq,Hq,D]; k_cache/v_cache [B,Tkv,Hkv,D] (Tkv = capacity);
+ * kv_lens = valid length per batch (NULL = Tkv). o [B,Tq,Hq,D] bf16;
+ * lse fp32 [B,Hq,Tq] or NULL. */
+attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache,
+                          void* o, float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Static description of a status code. */
+const char* attn_status_string(attn_status_t status);
+
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */
