@@ -1,7 +1,391 @@
-// Backward pass, bf16 (placeholder until the tiled kernels land).
+// Backward pass of fused exact attention, bf16, gfx950.
+//
+// Deterministic two-pass scheme without atomics (probjax pages,
+// "Attention performance", section "When to use which": the two-pass
+// kernels give bitwise reproducible gradients; "H100 (Hopper)", section
+// "Why": the split backward is the robust choice). With P recomputed from
+// the forward's LSE (the residuals are O and LSE only):
+//   pre-kernel:  D_i = sum_d dO_id O_id                       (attn_fp32.hip)
+//   dK/dV:       per (batch, KV head, 128-key tile), for each query head of
+//                the group and each 64-row query tile in ascending order:
+//                  S = Q K^T, P = exp2(S*c - LSE2), dP = dO V^T,
+//                  dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS
+//   dQ:          per (batch, head, 128-row query tile), for each 64-key tile:
+//                  S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D),
+//                  dQ^T += K^T dS^T
+// In both kernels the product whose accumulator becomes the next B operand
+// is arranged so the register layouts line up (see attn_device.hpp), and the
+// transposed operand (dO^T, Q^T, K^T) is read with the LDS transpose read.
+// KV tiles wholly past kv_len store zeros without running their loop.
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
 namespace attn {
-hipError_t launch_bwd_bf16(const BwdArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+void launch_delta_any(const BwdArgs& a, int D, bool bf16, hipStream_t s);
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ----------------------------------------------------------------- dK / dV
+
+template <int D>
+struct DkvCfg {
+  static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave
+  static constexpr int BM = 64;             // query rows per LDS tile
+  static constexpr int THREADS = 256;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int QSTRIDE = D + 8;     // LDS row stride of Q and dO tiles
+  static constexpr int TILE = BM * QSTRIDE;
+  static constexpr int CPR = D / 8;
+  static constexpr int CPT = BM * CPR / THREADS;
+  static_assert(BM * CPR % THREADS == 0, "tile must split evenly");
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
+  using C = DkvCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t q_s[C::TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t g_s[C::TILE];  // dO tile
+  __shared__ float lse_s[C::BM];
+  __shared__ float dlt_s[C::BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = bid % a.num_ktiles;
+  const int bkh = bid / a.num_ktiles;
+  const int kh = bkh % a.Hkv;
+  const int b = bkh / a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int k0 = kt * C::BN;
+  const int key = k0 + 32 * wave + l32;      // this lane's key
+
+  const long krs = (long)a.Hkv * D;
+  const long qrs = (long)a.Hq * D;
+  const long kvoff = ((long)b * a.Tkv * a.Hkv + kh) * D;
+  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
+
+  f32x16_t dk[C::DB], dv[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) {
+    dk[i] = f32x16_t{};
+    dv[i] = f32x16_t{};
+  }
+
+  if (k0 < kvlim) {
+    // K and V rows of this lane's key as B operands (k = head_dim).
+    u32x4_t kf[C::KS], vf[C::KS];
+    const bool key_ok = key < kvlim;
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) {
+      kf[t] = key_ok ? gload16((const uint16_t*)a.k + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+      vf[t] = key_ok ? gload16((const uint16_t*)a.v + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    }
+    const float c = a.scale_log2;
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int wave_min_key = k0 + 32 * wave;
+    const int wave_max_key = wave_min_key + 31;
+    const int qt_begin = a.causal ? k0 / C::BM : 0;
+    const int nqt = (a.Tq + C::BM - 1) / C::BM;
+
+    for (int g = 0; g < G; ++g) {
+      const int h = kh * G + g;
+      const uint16_t* qb = (const uint16_t*)a.q + ((long)b * a.Tq * a.Hq + h) * D;
+      const uint16_t* gb = (const uint16_t*)a.dout + ((long)b * a.Tq * a.Hq + h) * D;
+      const long stat0 = ((long)b * a.Hq + h) * a.Tq;
+      for (int qt = qt_begin; qt < nqt; ++qt) {
+        const int q0 = qt * C::BM;
+        __syncthreads();  // previous tile fully consumed
+#pragma unroll
+        for (int i = 0; i < C::CPT; ++i) {
+          const int ch = tid + C::THREADS * i;
+          const int row = ch / C::CPR, cc = ch % C::CPR;
+          const int qr = q0 + row;
+          u32x4_t x = u32x4_t{0, 0, 0, 0}, y = u32x4_t{0, 0, 0, 0};
+          if (qr < a.Tq) {
+            x = gload16(qb + qr * qrs + cc * 8);
+            y = gload16(gb + qr * qrs + cc * 8);
+          }
+          lds_write16(q_s + row * C::QSTRIDE + cc * 8, x);
+          lds_write16(g_s + row * C::QSTRIDE + cc * 8, y);
+        }
+        if (tid < C::BM) {
+          const int qr = q0 + tid;
+          lse_s[tid] = qr < a.Tq ? a.lse[stat0 + qr] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
+        } else if (tid < 2 * C::BM) {
+          const int qr = q0 + tid - C::BM;
+          dlt_s[tid - C::BM] = qr < a.Tq ? a.delta[stat0 + qr] : 0.f;
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int qb = 0; qb < C::BM / 32; ++qb) {
+          const int qmin = q0 + 32 * qb;
+          if (a.causal && qmin + 31 < wave_min_key) continue;  // every row precedes every key of this wave
+          const uint16_t* qrow_s = q_s + (32 * qb) * C::QSTRIDE;
+          const uint16_t* grow_s = g_s + (32 * qb) * C::QSTRIDE;
+          // S = Q K^T and dP = dO V^T: lane = key, registers = query rows.
+          f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+          for (int t = 0; t < C::KS; ++t) {
+            const u32x4_t qa = lds_read16(qrow_s + l32 * C::QSTRIDE + 16 * t + 8 * hh);
+            const u32x4_t ga = lds_read16(grow_s + l32 * C::QSTRIDE + 16 * t + 8 * hh);
+            s = mfma_bf16(qa, kf[t], s);
+            dp = mfma_bf16(ga, vf[t], dp);
+          }
+          const bool need_mask = (wave_max_key >= kvlim) || (a.causal && qmin < wave_max_key);
+          u32x4_t pb[2], dsb[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float pv[8], dsv[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+              const int r = 8 * u + x;
+              const int ql = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+              float p = fast_exp2(__builtin_fmaf(s[r], c, -lse_s[ql]));
+              if (need_mask) {
+                const bool ok = key < kvlim && (!a.causal || key <= q0 + ql);
+                p = ok ? p : 0.f;
+              }
+              pv[x] = p;
+              dsv[x] = p * (dp[r] - dlt_s[ql]);
+            }
+            pb[u] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                            pack_bf16(pv[6], pv[7])};
+            dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                             pack_bf16(dsv[6], dsv[7])};
+          }
+          // dV^T += dO^T P, dK^T += Q^T dS (k = query rows of this block).
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int roff = (16 * u + tr_row) * C::QSTRIDE + tr_col;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const u32x2_t g0 = lds_read_tr(grow_s + roff + 32 * db);
+              const u32x2_t g1 = lds_read_tr(grow_s + roff + 8 * C::QSTRIDE + 32 * db);
+              dv[db] = mfma_bf16(u32x4_t{g0[0], g0[1], g1[0], g1[1]}, pb[u], dv[db]);
+              const u32x2_t q0r = lds_read_tr(qrow_s + roff + 32 * db);
+              const u32x2_t q1r = lds_read_tr(qrow_s + roff + 8 * C::QSTRIDE + 32 * db);
+              dk[db] = mfma_bf16(u32x4_t{q0r[0], q0r[1], q1r[0], q1r[1]}, dsb[u], dk[db]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // Store: lane = key, register r of block db = head_dim 32*db + 8*(r/4) + 4*hh + r%4.
+  if (key < a.Tkv) {
+    uint16_t* dkp = (uint16_t*)a.dk + kvoff + key * krs;
+    uint16_t* dvp = (uint16_t*)a.dv + kvoff + key * krs;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hh;
+        *(u32x2_t*)(dkp + d) = u32x2_t{pack_bf16(dk[db][4 * g] * a.scale, dk[db][4 * g + 1] * a.scale),
+                                       pack_bf16(dk[db][4 * g + 2] * a.scale, dk[db][4 * g + 3] * a.scale)};
+        *(u32x2_t*)(dvp + d) = u32x2_t{pack_bf16(dv[db][4 * g], dv[db][4 * g + 1]),
+                                       pack_bf16(dv[db][4 * g + 2], dv[db][4 * g + 3])};
+      }
+  }
+}
+
+// --------------------------------------------------------------------- dQ
+
+template <int D>
+struct DqCfg {
+  static constexpr int BM = 128;            // query rows, 32 per wave
+  static constexpr int BN = 64;             // keys per tile
+  static constexpr int THREADS = 256;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int KSTRIDE = D + 8;
+  static constexpr int KTILE = BN * KSTRIDE;
+  static constexpr int CPR = D / 8;
+  static constexpr int CPT = BN * CPR / THREADS;
+  static_assert(BN * CPR % THREADS == 0, "tile must split evenly");
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * C::KTILE];  // [buf][K, V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int nqt = (a.Tq + C::BM - 1) / C::BM;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = nqt - 1 - (bid % nqt);
+  const int bh = bid / nqt;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+  const int kh = h / (a.Hq / a.Hkv);
+  const int q0 = qt * C::BM;
+
+  const long qrs = (long)a.Hq * D;
+  const long krs = (long)a.Hkv * D;
+  const long qoff = ((long)b * a.Tq * a.Hq + h) * D;
+  const uint16_t* kb = (const uint16_t*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
+  const uint16_t* vb = (const uint16_t*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
+
+  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
+  int kv_end = kvlim;
+  if (a.causal) kv_end = min(kv_end, q0 + C::BM);
+  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+
+  const int qrow = q0 + 32 * wave + l32;
+  const bool row_ok = qrow < a.Tq;
+  u32x4_t qf[C::KS], gf[C::KS];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) {
+    qf[t] = row_ok ? gload16((const uint16_t*)a.q + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    gf[t] = row_ok ? gload16((const uint16_t*)a.dout + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+  }
+  const long stat = ((long)b * a.Hq + h) * a.Tq + qrow;
+  const float lse2 = row_ok ? a.lse[stat] * kLog2e : INFINITY;
+  const float dlt = row_ok ? a.delta[stat] : 0.f;
+  const float c = a.scale_log2;
+
+  f32x16_t acc[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) acc[i] = f32x16_t{};
+
+  u32x4_t kr[C::CPT], vr[C::CPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int ch = tid + C::THREADS * i;
+      const int row = ch / C::CPR, cc = ch % C::CPR;
+      const int kk = k0 + row;
+      if (kk < kv_end) {
+        kr[i] = gload16(kb + kk * krs + cc * 8);
+        vr[i] = gload16(vb + kk * krs + cc * 8);
+      } else {
+        kr[i] = u32x4_t{0, 0, 0, 0};
+        vr[i] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* kl = lds + buf * 2 * C::KTILE;
+    uint16_t* vl = kl + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int ch = tid + C::THREADS * i;
+      const int row = ch / C::CPR, cc = ch % C::CPR;
+      lds_write16(kl + row * C::KSTRIDE + cc * 8, kr[i]);
+      lds_write16(vl + row * C::KSTRIDE + cc * 8, vr[i]);
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int wave_min_row = q0 + 32 * wave;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = it * C::BN;
+    if (it + 1 < ntiles) gload(k0 + C::BN);
+    const uint16_t* kl = lds + (it & 1) * 2 * C::KTILE;
+    const uint16_t* vl = kl + C::KTILE;
+
+    // S^T = K Q^T and dP^T = V dO^T: lane = query row, registers = keys.
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int off = (32 * j + l32) * C::KSTRIDE + 16 * t + 8 * hh;
+        s[j] = mfma_bf16(lds_read16(kl + off), qf[t], s[j]);
+        dp[j] = mfma_bf16(lds_read16(vl + off), gf[t], dp[j]);
+      }
+
+    const bool need_mask = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
+    u32x4_t dsb[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float dsv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int r = 8 * u + x;
+          float p = fast_exp2(__builtin_fmaf(s[j][r], c, -lse2));
+          if (need_mask) {
+            const int kk = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = kk < kvlim && (!a.causal || kk <= qrow);
+            p = ok ? p : 0.f;
+          }
+          dsv[x] = p * (dp[j][r] - dlt);
+        }
+        dsb[2 * j + u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                                 pack_bf16(dsv[6], dsv[7])};
+      }
+
+    // dQ^T += K^T dS^T (k = keys).
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint16_t* krow = kl + (16 * ks + tr_row) * C::KSTRIDE + tr_col;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const u32x2_t lo = lds_read_tr(krow + 32 * db);
+        const u32x2_t hi = lds_read_tr(krow + 8 * C::KSTRIDE + 32 * db);
+        acc[db] = mfma_bf16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, dsb[ks], acc[db]);
+      }
+    }
+
+    if (it + 1 < ntiles) lstore((it + 1) & 1);
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    uint16_t* dqp = (uint16_t*)a.dq + qoff + qrow * qrs;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hh;
+        *(u32x2_t*)(dqp + d) = u32x2_t{pack_bf16(acc[db][4 * g] * a.scale, acc[db][4 * g + 1] * a.scale),
+                                       pack_bf16(acc[db][4 * g + 2] * a.scale, acc[db][4 * g + 3] * a.scale)};
+      }
+  }
+}
+
+template <int D>
+void launch_bwd_kernels(const BwdArgs& a, hipStream_t s) {
+  const long kblocks = (long)a.num_ktiles * a.Hkv * a.B;
+  if (kblocks > 0) hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(256), 0, s, a);
+  const long nqt = (a.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+  const long qblocks = nqt * a.Hq * a.B;
+  if (qblocks > 0) hipLaunchKernelGGL(attn_dq_bf16_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int D, hipStream_t s) {
+  launch_delta_any(a, D, true, s);
+  if (D == 128)
+    launch_bwd_kernels<128>(a, s);
+  else
+    launch_bwd_kernels<64>(a, s);
+  return hipGetLastError();
+}
+
 }  // namespace attn

@@ -1,0 +1,77 @@
+"""Backward parity of the HIP kernels against the float64 oracle (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from forward_backward_amd.inputs import Case, workload_cases
+from helpers import TOL, device_inputs, rel_err, to_host64
+from test_gpu_fwd import SMALL
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(case, dev):
+    from forward_backward_amd import attn
+    o, lse = attn.fwd(dev["q"], dev["k"], dev["v"], scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"])
+    dq, dk, dv = attn.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale=case.scale, causal=case.causal,
+                          kv_lens=dev["kv_lens"])
+    return o, lse, dq, dk, dv
+
+
+def check_bwd(case, kv_heads=None):
+    import torch
+    host, dev, f64 = device_inputs(case)
+    print(f"[bwd] {case.name}", flush=True)
+    _, _, dq, dk, dv = run_fwd_bwd(case, dev)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.attention_bwd(f64["q"], f64["k"], f64["v"], f64["do"], case.scale, case.causal,
+                                         f64["kv_lens"], kv_heads=kv_heads)
+    gdq, gdk, gdv = to_host64(dq), to_host64(dk), to_host64(dv)
+    if kv_heads is not None:
+        G = case.Hq // case.Hkv
+        sel = lambda x, y: (np.stack([x[b, :, kh * G:(kh + 1) * G] for b, kh in kv_heads]),  # noqa: E731
+                            np.stack([y[b, :, kh * G:(kh + 1) * G] for b, kh in kv_heads]))
+        selk = lambda x, y: (np.stack([x[b, :, kh] for b, kh in kv_heads]),  # noqa: E731
+                             np.stack([y[b, :, kh] for b, kh in kv_heads]))
+        pairs = {"dq": sel(gdq, rdq), "dk": selk(gdk, rdk), "dv": selk(gdv, rdv)}
+    else:
+        pairs = {"dq": (gdq, rdq), "dk": (gdk, rdk), "dv": (gdv, rdv)}
+    for name, (g, r) in pairs.items():
+        err = rel_err(g, r)
+        print(f"    {name} rel err {err:.3e}", flush=True)
+        assert err <= TOL[case.dtype], f"{case.name}: {name} rel err {err:.3e}"
+    if case.kv_lens is not None:
+        for b, n in enumerate(case.kv_lens):
+            assert np.all(gdk[b, n:] == 0.0) and np.all(gdv[b, n:] == 0.0)
+            if n == 0:
+                assert np.all(gdq[b] == 0.0)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c.name)
+def test_bwd_small(case):
+    check_bwd(case)
+
+
+def test_bwd_fp32_correctness_workload():
+    (case,) = workload_cases(0)
+    check_bwd(case)
+
+
+@pytest.mark.parametrize("case", [c for c in workload_cases(1) if c.Tq in (600, 3000, 2048)], ids=lambda c: c.name)
+def test_bwd_bf16_d64_grid_sampled(case):
+    check_bwd(case, kv_heads=[(0, 0), (3, 7), (1, 4)])
+
+
+def test_bwd_is_bitwise_deterministic():
+    import torch
+    case = Case("d128_T333_causal_gqa_kvlen", 2, 333, 333, 8, 2, 128, causal=True, kv_lens=(333, 200),
+                workload_id=120)
+    host, dev, _ = device_inputs(case)
+    runs = [run_fwd_bwd(case, dev) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
