@@ -75,3 +75,16 @@ def test_bwd_is_bitwise_deterministic():
         for a, b in zip(runs[0], r):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+@pytest.mark.parametrize("case", workload_cases(2), ids=lambda c: c.name)
+def test_bwd_headline_T8192_sampled(case):
+    check_bwd(case, kv_heads=[(0, 0), (3, 5)])
+
+
+def test_bwd_kv_length_workload_sampled():
+    (case,) = workload_cases(3)
+    dq, dk, _ = check_bwd(case, kv_heads=[(0, 1), (1, 0), (2, 7), (3, 3)])
+    # Batch 0 has a single valid key: the exact dQ and dK are zero.
+    assert float(to_host64(dq[0]).__abs__().max()) <= 1e-3
+    assert float(to_host64(dk[0]).__abs__().max()) <= 1e-3

@@ -80,3 +80,13 @@ def test_fwd_is_deterministic():
     o2, l2 = run_fwd(case, dev)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("case", workload_cases(2), ids=lambda c: c.name)
+def test_fwd_headline_T8192_sampled(case):
+    check_case(case, heads=[(0, 0), (3, 5)])
+
+
+def test_fwd_kv_length_workload_sampled():
+    (case,) = workload_cases(3)
+    check_case(case, heads=[(0, 1), (1, 0), (2, 7), (3, 3)])
