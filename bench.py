@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of fused exact attention on one MI355X.
+
+Headline: forward + backward of bf16 multi-head attention, B=4, H=8,
+head_dim=128, Tq=Tkv=8192, non-causal, reported in TFLOP/s by the probjax
+pages' FLOP convention (forward 4*B*H*Tq*Tkv*D, halved for causal; forward +
+backward = 3.5x forward) and as a fraction of the bf16 MFMA peak.
+
+One step = attn_fwd followed by the three passes of attn_bwd on the same
+synthetic inputs (inputs resident in HBM before the timed region). W warmup
+steps, then exactly K timed steps between device synchronisations; HIP events
+around every kernel give the per-kernel average durations used for the
+roofline of the dominant kernel.
+
+Also reported (outside the main timed region): the causal variant of the same
+shape, and the split-KV GQA decode (B=4, 32 query heads over 8 KV heads,
+Tq=16, KV cache 16384, head_dim 128) against the HBM roofline, rotating four
+distinct K/V caches so that repeated calls cannot be served from the 256 MB
+Infinity Cache. The CPU baseline is the float64 oracle timed on this host's
+cores on a bounded sample of the headline workload.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s, bf16 B4 H8 d128 T8192; % of MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the causal and decode legs")
+    ap.add_argument("--decode-calls", type=int, default=200)
+    return ap.parse_args()
+
+
+def source_digest():
+    """Digest of the HIP sources: stored counter readings are only valid for the kernels they measured."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "forward_backward_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None if stale/missing."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("kernels", {}).get(kernel)
+    if not entry or rec.get("source_digest") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def device_tensors(case, seed=0, with_do=True):
+    import numpy as np
+    import torch
+    from forward_backward_amd import inputs as I
+
+    host = I.make_inputs(case, seed=seed, with_do=with_do)
+    dev = {}
+    for k, v in host.items():
+        if v is None:
+            dev[k] = None
+        elif k == "kv_lens":
+            dev[k] = torch.from_numpy(v).cuda()
+        else:
+            dev[k] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).cuda()
+    return host, dev
+
+
+def time_train_steps(case, steps, warmup):
+    """K timed fwd+bwd steps; returns (ms_per_step, {kernel: avg_ms})."""
+    import torch
+    from forward_backward_amd import attn
+
+    _, d = device_tensors(case)
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    kv = d["kv_lens"]
+    o = torch.empty_like(q)
+    lse = torch.empty((case.B, case.Hq, case.Tq), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = attn.bwd_workspace(q, k, case.causal, kv)
+    kw = dict(scale=case.scale, causal=case.causal, kv_lens=kv)
+
+    def step(ev=None):
+        attn.fwd(q, k, v, out=o, lse=lse, **kw)
+        if ev: ev[1].record()
+        attn.bwd_preprocess(o, do, ws, q, k, **kw)
+        if ev: ev[2].record()
+        attn.bwd_dkdv(q, k, v, lse, do, ws, dk, dv, **kw)
+        if ev: ev[3].record()
+        attn.bwd_dq(q, k, v, lse, do, ws, dq, **kw)
+        if ev: ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record()
+        step(evs[i])
+    torch.cuda.synchronize()
+    total = evs[0][0].elapsed_time(evs[-1][4])
+    names = ["attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    if not torch.isfinite(dq.float()).all() or not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite outputs in the benchmark step")
+    return total / steps, per
+
+
+def time_decode(case, calls, sets=4):
+    """Average ms per attn_decode call, rotating `sets` distinct K/V caches."""
+    import torch
+    from forward_backward_amd import attn
+
+    host, d0 = device_tensors(case, seed=0, with_do=False)
+    caches = [(d0["k"], d0["v"])]
+    for s in range(1, sets):
+        _, ds = device_tensors(case, seed=s, with_do=False)
+        caches.append((ds["k"], ds["v"]))
+    q, kv = d0["q"], d0["kv_lens"]
+    for i in range(4):
+        attn.decode(q, *caches[i % sets], kv_lens=kv, scale=case.scale)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(calls):
+        attn.decode(q, *caches[i % sets], kv_lens=kv, scale=case.scale)
+    e1.record()
+    torch.cuda.synchronize()
+    cold = e0.elapsed_time(e1) / calls
+    e0.record()
+    for i in range(calls):
+        attn.decode(q, *caches[0], kv_lens=kv, scale=case.scale)
+    e1.record()
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) / calls
+    return cold, warm, [int(x) for x in host["kv_lens"]]
+
+
+def cpu_baseline(case, seconds):
+    """The float64 oracle on a bounded sample: whole (batch, KV head) groups of the headline workload."""
+    import numpy as np
+    from forward_backward_amd import inputs as I
+    from forward_backward_amd.metrics import attention_flops
+    import oracle
+
+    host = I.make_inputs(case, seed=0)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+    groups = [(b, kh) for b in range(case.B) for kh in range(case.Hkv)]
+    done, t_used = 0, 0.0
+    for b, kh in groups:
+        sl = lambda x: I.to_float64(x[b:b + 1, :, kh:kh + 1], case.dtype)  # noqa: E731
+        q, k, v, do = sl(host["q"]), sl(host["k"]), sl(host["v"]), sl(host["do"])
+        t0 = time.perf_counter()
+        oracle.attention_fwd(q, k, v, case.scale, case.causal)
+        oracle.attention_bwd(q, k, v, do, case.scale, case.causal)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= seconds:
+            break
+    flops = attention_flops(1, done, case.Tq, case.Tkv, case.D, case.causal, "fwd_bwd")
+    return {
+        "value": flops / t_used / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(groups)} (batch, head) groups of B4 H8 d128 T8192 non-causal, fwd then bwd, "
+                  f"float64 NumPy, {t_used:.1f} s",
+        "seconds": t_used,
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from forward_backward_amd import attn
+    from forward_backward_amd.inputs import workload_cases
+    from forward_backward_amd.metrics import PEAK_HBM_GBS, PEAK_TFLOPS, attention_flops, decode_bytes
+
+    attn.lib()  # fail loudly without the HIP library
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs {props.multi_processor_count}")
+
+    full, causal = workload_cases(2)
+    log(f"headline {full.name}: warmup {args.warmup}, steps {args.steps}")
+    ms, per = time_train_steps(full, args.steps, args.warmup)
+    flops = attention_flops(full.B, full.Hq, full.Tq, full.Tkv, full.D, False, "fwd_bwd")
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"  {ms:.3f} ms/step, {tflops:.1f} TFLOP/s; per kernel ms: " +
+        ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
+
+    fwd_f = attention_flops(full.B, full.Hq, full.Tq, full.Tkv, full.D, False, "fwd")
+    kernel_flops = {"attn_fwd": fwd_f, "bwd_dkdv": 2 * fwd_f, "bwd_dq": 1.5 * fwd_f}
+    kernel_symbol = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_dkdv": "attn_dkdv_bf16_kernel",
+                     "bwd_dq": "attn_dq_bf16_kernel"}
+    dom = max(kernel_flops, key=lambda n: per[n])
+    achieved = kernel_flops[dom] / (per[dom] * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": kernel_symbol[dom],
+        "achieved": round(achieved, 2),
+        "peak": PEAK_TFLOPS["bf16"],
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+        "traffic": stored_traffic(kernel_symbol[dom]),
+        "avg_ms": round(per[dom], 4),
+        "flops_per_launch": kernel_flops[dom],
+    }
+
+    extra = {}
+    if not args.no_extra:
+        log(f"causal {causal.name}")
+        cms, cper = time_train_steps(causal, args.steps, 1)
+        cfl = attention_flops(causal.B, causal.Hq, causal.Tq, causal.Tkv, causal.D, True, "fwd_bwd")
+        extra["causal"] = {"ms_per_step": round(cms, 4), "tflops": round(cfl / (cms * 1e-3) / 1e12, 2),
+                           "per_kernel_ms": {k: round(v, 4) for k, v in cper.items()}}
+        log(f"  {cms:.3f} ms/step, {extra['causal']['tflops']} TFLOP/s")
+        (dec,) = workload_cases(4)
+        cold, warm, lens = time_decode(dec, args.decode_calls)
+        nbytes = decode_bytes(dec.B, dec.Tq, dec.Hq, dec.Hkv, dec.D, lens)
+        gbs = nbytes / (cold * 1e-3) / 1e9
+        extra["decode"] = {
+            "workload": dec.name, "kv_lens": lens, "us_per_call": round(cold * 1e3, 2),
+            "us_per_call_same_cache": round(warm * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": nbytes},
+        }
+        log(f"decode {cold * 1e3:.1f} us/call (rotating caches), {warm * 1e3:.1f} us same cache, {gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (float64 oracle)")
+        cpu = cpu_baseline(full, args.cpu_seconds)
+        log(f"  {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) bf16 from seed 0",
+        "config": {"workload": "bf16 MHA fwd+bwd B4 H8 d128 Tq=Tkv=8192 non-causal", "B": 4, "H": 8, "D": 128,
+                   "T": 8192, "causal": False},
+        "mfma_peak_frac": round(tflops / PEAK_TFLOPS["bf16"], 4),
+        "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -56,6 +56,9 @@ _SIGS = {
     "attn_fwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_P]),
     "attn_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "attn_bwd_preprocess": (ctypes.c_int, [_P, _V, _V, _V, ctypes.c_size_t, _V]),
+    "attn_bwd_dkdv": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "attn_bwd_dq": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "attn_decode_num_splits": (ctypes.c_int32, [_P]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [_P, ctypes.c_int32]),
     "attn_decode": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_int32, _V, ctypes.c_size_t, _V]),
@@ -151,6 +154,33 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_lens=None, workspace=N
     _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
                           _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
     return dq, dk, dv
+
+
+def bwd_workspace(q, k, causal=False, kv_lens=None):
+    """A device workspace large enough for the backward of this problem."""
+    p = _params_for(q, k, None, causal, kv_lens)
+    need = lib().attn_bwd_workspace_size(ctypes.byref(p))
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+
+
+def bwd_preprocess(o, do, ws, q, k, scale=None, causal=False, kv_lens=None):
+    """Pass 1 of the backward: D = rowsum(dO * O) into the workspace."""
+    p = _params_for(q, k, scale, causal, kv_lens)
+    _check(lib().attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(do), _ptr(ws), ws.numel(), _stream()))
+
+
+def bwd_dkdv(q, k, v, lse, do, ws, dk, dv, scale=None, causal=False, kv_lens=None):
+    """Pass 2 of the backward: dK and dV (needs the preprocess pass done)."""
+    p = _params_for(q, k, scale, causal, kv_lens)
+    _check(lib().attn_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
+                               _ptr(ws), ws.numel(), _stream()))
+
+
+def bwd_dq(q, k, v, lse, do, ws, dq, scale=None, causal=False, kv_lens=None):
+    """Pass 3 of the backward: dQ (needs the preprocess pass done)."""
+    p = _params_for(q, k, scale, causal, kv_lens)
+    _check(lib().attn_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq), _ptr(ws),
+                             ws.numel(), _stream()))
 
 
 def decode(q, k_cache, v_cache, kv_lens=None, scale=None, num_splits=0, want_lse=True):

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "attn_internal.h"
 
@@ -33,8 +34,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr long kMaxGrid = 2147483647L;
 constexpr float kLog2e = 1.4426950408889634f;
-
-int elem_bytes(const attn_params_t* p) { return p->dtype == ATTN_FP32 ? 4 : 2; }
 
 size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
@@ -95,29 +94,100 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   return ok();
 }
 
-attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v, const void* o,
-                       const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared checks and argument setup of the backward entry points; each entry
+// point then checks and fills the tensors its passes touch.
+attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws, size_t ws_bytes) {
   attn_status_t st = attn_validate(p, ATTN_OP_BWD);
   if (st != ATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return fail(ATTN_ERR_INVALID, "null tensor pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv))
-    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
   const size_t need = attn_bwd_workspace_size(p);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "workspace too small (%d bytes needed)", (int)need);
-  attn::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = static_cast<float*>(workspace); a.kv_lens = p->kv_lens;
+  std::memset(&a, 0, sizeof(a));
+  a.delta = static_cast<float*>(const_cast<void*>(ws));
+  a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
   a.num_qtiles = (p->Tq + attn::kBwdBlockM - 1) / attn::kBwdBlockM;
   a.num_ktiles = (p->Tkv + attn::kBwdBlockN - 1) / attn::kBwdBlockN;
+  return ATTN_OK;
+}
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* x : ps)
+    if (!aligned16(x)) return false;
+  return true;
+}
+
+bool none_null(std::initializer_list<const void*> ps) {
+  for (const void* x : ps)
+    if (x == nullptr) return false;
+  return true;
+}
+
+attn_status_t run_pass(const attn_params_t* p, const attn::BwdArgs& a, int pass, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = p->dtype == ATTN_BF16 ? attn::launch_bwd_bf16(a, p->D, s) : attn::launch_bwd_fp32(a, p->D, s);
-  if (e == hipErrorNotSupported) return fail(ATTN_ERR_UNSUPPORTED, "no kernel for this configuration");
+  hipError_t e = p->dtype == ATTN_BF16 ? attn::launch_bwd_pass_bf16(a, p->D, pass, s)
+                                       : attn::launch_bwd_pass_fp32(a, p->D, pass, s);
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const void* dout, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  attn::BwdArgs a;
+  attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!none_null({o, dout})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!all_aligned({o, dout})) return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  a.o = o; a.dout = dout;
+  return run_pass(p, a, attn::kBwdPre, stream);
+}
+
+attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
+                            const void* dout, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  attn::BwdArgs a;
+  attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!none_null({q, k, v, lse, dout, dk, dv})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!all_aligned({q, k, v, dout, dk, dv})) return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  a.q = q; a.k = k; a.v = v; a.lse = lse; a.dout = dout; a.dk = dk; a.dv = dv;
+  return run_pass(p, a, attn::kBwdDkdv, stream);
+}
+
+attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
+                          const void* dout, void* dq, const void* workspace, size_t workspace_bytes, void* stream) {
+  attn::BwdArgs a;
+  attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!none_null({q, k, v, lse, dout, dq})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!all_aligned({q, k, v, dout, dq})) return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  a.q = q; a.k = k; a.v = v; a.lse = lse; a.dout = dout; a.dq = dq;
+  return run_pass(p, a, attn::kBwdDq, stream);
+}
+
+attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  attn::BwdArgs a;
+  attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (!none_null({q, k, v, o, lse, dout, dq, dk, dv})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!all_aligned({q, k, v, o, dout, dq, dk, dv}))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  for (int pass : {attn::kBwdPre, attn::kBwdDkdv, attn::kBwdDq}) {
+    st = run_pass(p, a, pass, stream);
+    if (st != ATTN_OK) return st;
+  }
   return ok();
 }
 

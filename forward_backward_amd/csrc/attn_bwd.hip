@@ -369,22 +369,26 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
 }
 
 template <int D>
-void launch_bwd_kernels(const BwdArgs& a, hipStream_t s) {
-  const long kblocks = (long)a.num_ktiles * a.Hkv * a.B;
-  if (kblocks > 0) hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(256), 0, s, a);
-  const long nqt = (a.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
-  const long qblocks = nqt * a.Hq * a.B;
-  if (qblocks > 0) hipLaunchKernelGGL(attn_dq_bf16_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
+void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
+  if (pass == kBwdPre) {
+    launch_delta_any(a, D, true, s);
+  } else if (pass == kBwdDkdv) {
+    const long kblocks = (long)a.num_ktiles * a.Hkv * a.B;
+    if (kblocks > 0) hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(256), 0, s, a);
+  } else {
+    const long nqt = (a.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+    const long qblocks = nqt * a.Hq * a.B;
+    if (qblocks > 0) hipLaunchKernelGGL(attn_dq_bf16_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int D, hipStream_t s) {
-  launch_delta_any(a, D, true, s);
+hipError_t launch_bwd_pass_bf16(const BwdArgs& a, int D, int pass, hipStream_t s) {
   if (D == 128)
-    launch_bwd_kernels<128>(a, s);
+    launch_pass<128>(a, pass, s);
   else
-    launch_bwd_kernels<64>(a, s);
+    launch_pass<64>(a, pass, s);
   return hipGetLastError();
 }
 

@@ -237,21 +237,25 @@ hipError_t launch_fwd_fp32(const FwdArgs& a, int D, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_fp32(const BwdArgs& a, int D, hipStream_t s) {
-  launch_delta_any(a, D, false, s);
-  const long qrows = (long)a.B * a.Hq * a.Tq;
-  const long krows = (long)a.B * a.Hkv * a.Tkv;
-  if (krows > 0) {
-    if (D == 128)
-      hipLaunchKernelGGL(attn_dkdv_fp32_kernel<128>, dim3((unsigned)krows), dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_dkdv_fp32_kernel<64>, dim3((unsigned)krows), dim3(64), 0, s, a);
-  }
-  if (qrows > 0) {
-    if (D == 128)
-      hipLaunchKernelGGL(attn_dq_fp32_kernel<128>, dim3((unsigned)qrows), dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL(attn_dq_fp32_kernel<64>, dim3((unsigned)qrows), dim3(64), 0, s, a);
+hipError_t launch_bwd_pass_fp32(const BwdArgs& a, int D, int pass, hipStream_t s) {
+  if (pass == kBwdPre) {
+    launch_delta_any(a, D, false, s);
+  } else if (pass == kBwdDkdv) {
+    const long krows = (long)a.B * a.Hkv * a.Tkv;
+    if (krows > 0) {
+      if (D == 128)
+        hipLaunchKernelGGL(attn_dkdv_fp32_kernel<128>, dim3((unsigned)krows), dim3(64), 0, s, a);
+      else
+        hipLaunchKernelGGL(attn_dkdv_fp32_kernel<64>, dim3((unsigned)krows), dim3(64), 0, s, a);
+    }
+  } else {
+    const long qrows = (long)a.B * a.Hq * a.Tq;
+    if (qrows > 0) {
+      if (D == 128)
+        hipLaunchKernelGGL(attn_dq_fp32_kernel<128>, dim3((unsigned)qrows), dim3(64), 0, s, a);
+      else
+        hipLaunchKernelGGL(attn_dq_fp32_kernel<64>, dim3((unsigned)qrows), dim3(64), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

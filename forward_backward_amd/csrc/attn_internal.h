@@ -63,8 +63,10 @@ struct DecodeArgs {
 // Launchers (each returns the hipGetLastError() after its launches).
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, hipStream_t s);
 hipError_t launch_fwd_fp32(const FwdArgs& a, int D, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int D, hipStream_t s);
-hipError_t launch_bwd_fp32(const BwdArgs& a, int D, hipStream_t s);
+// Backward passes: 0 = D pre-kernel, 1 = dK/dV, 2 = dQ.
+enum BwdPass { kBwdPre = 0, kBwdDkdv = 1, kBwdDq = 2 };
+hipError_t launch_bwd_pass_bf16(const BwdArgs& a, int D, int pass, hipStream_t s);
+hipError_t launch_bwd_pass_fp32(const BwdArgs& a, int D, int pass, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s);
 
 // Tile sizes the host needs for grids and workspaces.

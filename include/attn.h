@@ -94,6 +94,19 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* The three passes of attn_bwd as separate calls, in the order attn_bwd
+ * runs them. attn_bwd_preprocess writes D = rowsum(dO * O) into the
+ * workspace; attn_bwd_dkdv and attn_bwd_dq read it and are independent of
+ * each other, so a caller may run them on two streams once the
+ * preprocess has completed. Arguments mean what they mean for attn_bwd. */
+attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const void* dout, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
+                            const void* dout, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                            void* stream);
+attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
+                          const void* dout, void* dq, const void* workspace, size_t workspace_bytes, void* stream);
+
 /* Split count attn_decode uses when num_splits = 0 (a pure function of the
  * shape, so reruns are bitwise identical). */
 int32_t attn_decode_num_splits(const attn_params_t* p);

@@ -89,6 +89,12 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.attn_bwd(ctypes.byref(p), *args, None, 0, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), *args, FAKE, need - 1, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), None, *args[1:], FAKE, need, None) == attn.ATTN_ERR_INVALID
+    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, need - 1, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_bwd_preprocess(ctypes.byref(p), None, FAKE, FAKE, need, None) == attn.ATTN_ERR_INVALID
+    assert L.attn_bwd_dkdv(ctypes.byref(p), *([FAKE] * 7), None, 0, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_bwd_dkdv(ctypes.byref(p), *([FAKE] * 6), None, FAKE, need, None) == attn.ATTN_ERR_INVALID
+    assert L.attn_bwd_dq(ctypes.byref(p), *([FAKE] * 6), FAKE, need - 4, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_bwd_dq(ctypes.byref(p), MISALIGNED, *([FAKE] * 5), FAKE, need, None) == attn.ATTN_ERR_INVALID
     d = P(Tq=16, Tkv=16384, Hq=32, Hkv=8)
     s = L.attn_decode_num_splits(ctypes.byref(d))
     assert s >= 2
