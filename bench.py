@@ -51,6 +51,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the causal and decode legs")
     ap.add_argument("--decode-calls", type=int, default=200)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of this many MiB (reference dispatch for HBM counters)")
     return ap.parse_args()
 
 
@@ -222,6 +224,16 @@ def main():
         sys.exit(1)
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs {props.multi_processor_count}")
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes")
+        del src, dst
 
     full, causal = workload_cases(2)
     log(f"headline {full.name}: warmup {args.warmup}, steps {args.steps}")

@@ -11,7 +11,9 @@
 //                    and 16 of the 32 keys of each key block, the other 16 in
 //                    lane l^32;
 //   softmax          row max over the lane's values plus one half-swap; base-2
-//                    exponentials with the scale folded into one FMA;
+//                    exponentials with the scale folded into one FMA; O and
+//                    the row sum are rescaled only when a row max grows by
+//                    more than 2^8 (wave-uniform decision);
 //   O^T += V^T P^T   (32x32x16 MFMA; P is converted from the S accumulator
 //                    registers directly, V is read with the LDS transpose read
 //                    so its key order matches the registers of P).
@@ -26,6 +28,8 @@
 namespace attn {
 namespace {
 
+constexpr float kRescaleLog2 = 8.f;  // rescale O only when a row max grows by > 2^8
+
 template <int D>
 struct FwdCfg {
   static constexpr int BM = kFwdBlockM;       // 128 query rows
@@ -34,7 +38,7 @@ struct FwdCfg {
   static constexpr int KS = D / 16;           // MFMA k-steps over head_dim
   static constexpr int DB = D / 32;           // 32-wide blocks of head_dim in O
   static constexpr int KSTRIDE = D + 8;       // LDS row stride of K (elements)
-  static constexpr int VSTRIDE = D + 16;      // LDS row stride of V (elements)
+  static constexpr int VSTRIDE = D + 32;      // LDS row stride of V (elements)
   static constexpr int KTILE = BN * KSTRIDE;
   static constexpr int VTILE = BN * VSTRIDE;
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
@@ -43,7 +47,7 @@ struct FwdCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::KTILE + C::VTILE)];
 
@@ -165,10 +169,20 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[j][r]);
     mt = half_max(mt);
-    const float mnew = fmaxf(m, mt);
-    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mref) * c);
-    const float nb = -mref * c;
+    // Lazy rescaling: the reference max m only moves when some row of the
+    // wave would otherwise see exponentials above 2^kRescaleLog2 (or had no
+    // valid key yet). Numerator and denominator share the reference, so the
+    // result is the same; it only bounds P (kept <= 2^8, exact in bf16's range).
+    const bool grow = (m == -INFINITY) ? (mt != -INFINITY) : ((mt - m) * c > kRescaleLog2);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mnew) * c);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
+      m = mnew;
+    }
+    const float nb = (m == -INFINITY) ? 0.f : -m * c;
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -178,10 +192,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
         s[j][r] = p;
         ps += p;
       }
-    lsum = lsum * alpha + ps;
-    m = mnew;
-#pragma unroll
-    for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
+    lsum += ps;
 
     // P (bf16) as the B operand of O^T += V^T P^T, one operand per 16 keys.
     u32x4_t pf[4];
