@@ -115,7 +115,7 @@ def time_train_steps(case, steps, warmup):
     def step(ev=None):
         attn.fwd(q, k, v, out=o, lse=lse, **kw)
         if ev: ev[1].record()
-        attn.bwd_preprocess(o, do, ws, q, k, **kw)
+        attn.bwd_preprocess(o, lse, do, ws, q, k, **kw)
         if ev: ev[2].record()
         attn.bwd_dkdv(q, k, v, lse, do, ws, dk, dv, **kw)
         if ev: ev[3].record()

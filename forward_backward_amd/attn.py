@@ -56,7 +56,7 @@ _SIGS = {
     "attn_fwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
     "attn_bwd_workspace_size": (ctypes.c_size_t, [_P]),
     "attn_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
-    "attn_bwd_preprocess": (ctypes.c_int, [_P, _V, _V, _V, ctypes.c_size_t, _V]),
+    "attn_bwd_preprocess": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "attn_bwd_dkdv": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "attn_bwd_dq": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "attn_decode_num_splits": (ctypes.c_int32, [_P]),
@@ -163,10 +163,11 @@ def bwd_workspace(q, k, causal=False, kv_lens=None):
     return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
 
 
-def bwd_preprocess(o, do, ws, q, k, scale=None, causal=False, kv_lens=None):
-    """Pass 1 of the backward: D = rowsum(dO * O) into the workspace."""
+def bwd_preprocess(o, lse, do, ws, q, k, scale=None, causal=False, kv_lens=None):
+    """Pass 1 of the backward: D = rowsum(dO * O) and LSE * log2(e) into the workspace."""
     p = _params_for(q, k, scale, causal, kv_lens)
-    _check(lib().attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(do), _ptr(ws), ws.numel(), _stream()))
+    _check(lib().attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(lse), _ptr(do), _ptr(ws), ws.numel(),
+                                     _stream()))
 
 
 def bwd_dkdv(q, k, v, lse, do, ws, dk, dv, scale=None, causal=False, kv_lens=None):

@@ -63,10 +63,15 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   return ok();
 }
 
-size_t attn_bwd_workspace_size(const attn_params_t* p) {
-  if (p == nullptr) return 0;
+// fp32 [B, Hq, Tq] row statistics per array.
+static size_t bwd_stat_bytes(const attn_params_t* p) {
   return round_up((size_t)(p->B > 0 ? p->B : 0) * (p->Hq > 0 ? p->Hq : 0) * (p->Tq > 0 ? p->Tq : 0) * sizeof(float),
                   256);
+}
+
+size_t attn_bwd_workspace_size(const attn_params_t* p) {
+  if (p == nullptr) return 0;
+  return 2 * bwd_stat_bytes(p);
 }
 
 attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -108,6 +113,7 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
     return fail(ATTN_ERR_WORKSPACE, "workspace too small (%d bytes needed)", (int)need);
   std::memset(&a, 0, sizeof(a));
   a.delta = static_cast<float*>(const_cast<void*>(ws));
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ws)) + bwd_stat_bytes(p));
   a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
@@ -140,14 +146,14 @@ attn_status_t run_pass(const attn_params_t* p, const attn::BwdArgs& a, int pass,
 
 extern "C" {
 
-attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const void* dout, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const float* lse, const void* dout,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   attn::BwdArgs a;
   attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  if (!none_null({o, dout})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
+  if (!none_null({o, lse, dout})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
   if (!all_aligned({o, dout})) return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
-  a.o = o; a.dout = dout;
+  a.o = o; a.lse = lse; a.dout = dout;
   return run_pass(p, a, attn::kBwdPre, stream);
 }
 

@@ -32,24 +32,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <int D>
 struct DkvCfg {
   static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave
-  static constexpr int BM = 64;             // query rows per LDS tile
+  static constexpr int BM = 64;             // query rows per LDS tile (2 blocks of 32)
   static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int QSTRIDE = D + 8;     // LDS row stride of Q and dO tiles
-  static constexpr int TILE = BM * QSTRIDE;
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = BM * CPR / THREADS;
-  static_assert(BM * CPR % THREADS == 0, "tile must split evenly");
+  static constexpr int TILE = BM * D;       // swizzled, unpadded (read row-wise and transposed)
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   using C = DkvCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[C::TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t g_s[C::TILE];  // dO tile
-  __shared__ float lse_s[C::BM];
-  __shared__ float dlt_s[C::BM];
+  // Two pipeline stages of the Q and dO tiles in one array, so that one
+  // per-lane offset plus a constant addresses every stage.
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * C::TILE];
+  __shared__ __attribute__((aligned(16))) float stats[4 * C::BM];
+  uint16_t* const q_s0 = tiles;
+  uint16_t* const g_s0 = tiles + C::TILE;   // dO tiles
+  uint16_t* const q_s1 = tiles + 2 * C::TILE;
+  uint16_t* const g_s1 = tiles + 3 * C::TILE;
+  float* const l_s0 = stats;                // LSE * log2(e)
+  float* const d_s0 = stats + C::BM;        // D = rowsum(dO * O)
+  float* const l_s1 = stats + 2 * C::BM;
+  float* const d_s1 = stats + 3 * C::BM;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,90 +98,150 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
     const int wave_max_key = wave_min_key + 31;
     const int qt_begin = a.causal ? k0 / C::BM : 0;
     const int nqt = (a.Tq + C::BM - 1) / C::BM;
+    const int nq = nqt - qt_begin;
+    const int ntiles = G * nq;  // (query head, query tile) pairs in a fixed order
 
-    for (int g = 0; g < G; ++g) {
-      const int h = kh * G + g;
-      const uint16_t* qb = (const uint16_t*)a.q + ((long)b * a.Tq * a.Hq + h) * D;
-      const uint16_t* gb = (const uint16_t*)a.dout + ((long)b * a.Tq * a.Hq + h) * D;
+    // Per-lane swizzled offsets (elements). swz_f depends only on the low 4 bits
+    // of the row, so rows 32*qb + l32 and 32*qb + 16*u + tr_row (+8) share them;
+    // the row block and stage parts are compile-time constants.
+    int nrm[C::KS], trd[C::DB][2];
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      trd[db][0] = swz_off<D>(tr_row, 32 * db + tr_col);
+      trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col);
+    }
+
+    auto issue = [&](int idx, uint16_t* qs, uint16_t* gs, float* ls, float* ds) {
+      const int h = kh * G + idx / nq;
+      const int q0 = (qt_begin + idx % nq) * C::BM;
+      const long hoff = ((long)b * a.Tq * a.Hq + h) * D;
+      dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
+      dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
       const long stat0 = ((long)b * a.Hq + h) * a.Tq;
-      for (int qt = qt_begin; qt < nqt; ++qt) {
-        const int q0 = qt * C::BM;
-        __syncthreads();  // previous tile fully consumed
-#pragma unroll
-        for (int i = 0; i < C::CPT; ++i) {
-          const int ch = tid + C::THREADS * i;
-          const int row = ch / C::CPR, cc = ch % C::CPR;
-          const int qr = q0 + row;
-          u32x4_t x = u32x4_t{0, 0, 0, 0}, y = u32x4_t{0, 0, 0, 0};
-          if (qr < a.Tq) {
-            x = gload16(qb + qr * qrs + cc * 8);
-            y = gload16(gb + qr * qrs + cc * 8);
-          }
-          lds_write16(q_s + row * C::QSTRIDE + cc * 8, x);
-          lds_write16(g_s + row * C::QSTRIDE + cc * 8, y);
-        }
-        if (tid < C::BM) {
-          const int qr = q0 + tid;
-          lse_s[tid] = qr < a.Tq ? a.lse[stat0 + qr] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
-        } else if (tid < 2 * C::BM) {
-          const int qr = q0 + tid - C::BM;
-          dlt_s[tid - C::BM] = qr < a.Tq ? a.delta[stat0 + qr] : 0.f;
-        }
-        __syncthreads();
+      if (wave == 0) dma_row64(ls, a.lse2 + stat0, q0, a.Tq, lane);
+      if (wave == 1) dma_row64(ds, a.delta + stat0, q0, a.Tq, lane);
+    };
 
+    auto compute = [&](int idx, const uint16_t* qsb, const uint16_t* gsb, const float* ls, const float* ds,
+                       auto&& issue_next) {
+      const int q0 = (qt_begin + idx % nq) * C::BM;
+      bool issued = false;
 #pragma unroll
-        for (int qb = 0; qb < C::BM / 32; ++qb) {
-          const int qmin = q0 + 32 * qb;
-          if (a.causal && qmin + 31 < wave_min_key) continue;  // every row precedes every key of this wave
-          const uint16_t* qrow_s = q_s + (32 * qb) * C::QSTRIDE;
-          const uint16_t* grow_s = g_s + (32 * qb) * C::QSTRIDE;
-          // S = Q K^T and dP = dO V^T: lane = key, registers = query rows.
-          f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-          for (int t = 0; t < C::KS; ++t) {
-            const u32x4_t qa = lds_read16(qrow_s + l32 * C::QSTRIDE + 16 * t + 8 * hh);
-            const u32x4_t ga = lds_read16(grow_s + l32 * C::QSTRIDE + 16 * t + 8 * hh);
-            s = mfma_bf16(qa, kf[t], s);
-            dp = mfma_bf16(ga, vf[t], dp);
+      for (int qb = 0; qb < C::BM / 32; ++qb) {
+        const int qmin = q0 + 32 * qb;
+        // A skipped block still lets the next tile's loads start.
+        if (qmin >= a.Tq || (a.causal && qmin + 31 < wave_min_key)) {
+          if (!issued) {
+            issue_next();
+            issued = true;
           }
-          const bool need_mask = (wave_max_key >= kvlim) || (a.causal && qmin < wave_max_key);
-          u32x4_t pb[2], dsb[2];
+          continue;
+        }
+        const uint16_t* qrow = qsb + 32 * qb * D;
+        const uint16_t* grow = gsb + 32 * qb * D;
+        // Fragments of the block, all requested before the first product so
+        // that the LDS latency is paid once per block rather than per product.
+        u32x4_t qa[C::KS], ga[C::KS];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float pv[8], dsv[8];
+        for (int t = 0; t < C::KS; ++t) {
+          qa[t] = lds_read16(qrow + nrm[t]);
+          ga[t] = lds_read16(grow + nrm[t]);
+        }
+        // Row statistics of the 16 query rows this lane's registers cover.
+        f32x4_t lv[4], dl[4];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              const int r = 8 * u + x;
-              const int ql = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-              float p = fast_exp2(__builtin_fmaf(s[r], c, -lse_s[ql]));
-              if (need_mask) {
-                const bool ok = key < kvlim && (!a.causal || key <= q0 + ql);
-                p = ok ? p : 0.f;
-              }
-              pv[x] = p;
-              dsv[x] = p * (dp[r] - dlt_s[ql]);
-            }
-            pb[u] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                            pack_bf16(pv[6], pv[7])};
-            dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                             pack_bf16(dsv[6], dsv[7])};
-          }
-          // dV^T += dO^T P, dK^T += Q^T dS (k = query rows of this block).
+        for (int g = 0; g < 4; ++g) {
+          lv[g] = *(const f32x4_t*)(ls + 32 * qb + 8 * g + 4 * hh);
+          dl[g] = *(const f32x4_t*)(ds + 32 * qb + 8 * g + 4 * hh);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // S = Q K^T and dP = dO V^T: lane = key, registers = query rows.
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int roff = (16 * u + tr_row) * C::QSTRIDE + tr_col;
+        for (int t = 0; t < C::KS; ++t) {
+          s = mfma_bf16(qa[t], kf[t], s);
+          dp = mfma_bf16(ga[t], vf[t], dp);
+        }
+        // Transposed fragments for dV and dK, requested while S and dP run.
+        u32x2_t gt[2][C::DB][2], xt[2][C::DB][2];
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-              const u32x2_t g0 = lds_read_tr(grow_s + roff + 32 * db);
-              const u32x2_t g1 = lds_read_tr(grow_s + roff + 8 * C::QSTRIDE + 32 * db);
-              dv[db] = mfma_bf16(u32x4_t{g0[0], g0[1], g1[0], g1[1]}, pb[u], dv[db]);
-              const u32x2_t q0r = lds_read_tr(qrow_s + roff + 32 * db);
-              const u32x2_t q1r = lds_read_tr(qrow_s + roff + 8 * C::QSTRIDE + 32 * db);
-              dk[db] = mfma_bf16(u32x4_t{q0r[0], q0r[1], q1r[0], q1r[1]}, dsb[u], dk[db]);
-            }
+        for (int u = 0; u < 2; ++u) {
+          const uint16_t* gblk = gsb + (32 * qb + 16 * u) * D;
+          const uint16_t* qblk = qsb + (32 * qb + 16 * u) * D;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            gt[u][db][0] = lds_read_tr(gblk + trd[db][0]);
+            gt[u][db][1] = lds_read_tr(gblk + trd[db][1]);
+            xt[u][db][0] = lds_read_tr(qblk + trd[db][0]);
+            xt[u][db][1] = lds_read_tr(qblk + trd[db][1]);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // The next tile's loads start here: the compiler cannot tell them from
+        // the transpose reads, so transpose reads issued while they are in
+        // flight wait for them; from here to the next block's transpose reads
+        // is a whole block of matrix work.
+        if (!issued) {
+          issue_next();
+          issued = true;
+        }
+        const bool need_mask =
+            (wave_max_key >= kvlim) || (a.causal && qmin < wave_max_key) || (qmin + 31 >= a.Tq);
+        u32x4_t pb[2], dsb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float pv[8], dsv[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int r = 8 * u + x;
+            const int ql = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            float p = fast_exp2(__builtin_fmaf(s[r], c, -lv[r >> 2][r & 3]));
+            if (need_mask) {
+              const bool ok = (key < kvlim) & (!a.causal | (key <= q0 + ql)) & (q0 + ql < a.Tq);
+              p = ok ? p : 0.f;
+            }
+            pv[x] = p;
+            dsv[x] = p * (dp[r] - dl[r >> 2][r & 3]);
+          }
+          pb[u] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                          pack_bf16(pv[6], pv[7])};
+          dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                           pack_bf16(dsv[6], dsv[7])};
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS (k = query rows of this block).
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            dv[db] = mfma_bf16(u32x4_t{gt[u][db][0][0], gt[u][db][0][1], gt[u][db][1][0], gt[u][db][1][1]}, pb[u],
+                               dv[db]);
+            dk[db] = mfma_bf16(u32x4_t{xt[u][db][0][0], xt[u][db][0][1], xt[u][db][1][0], xt[u][db][1][1]}, dsb[u],
+                               dk[db]);
+          }
       }
+      if (!issued) issue_next();
+    };
+
+    // One pipeline step: compute tile idx from stage `c*` and, part-way
+    // through, start loading tile idx + 1 (if any) into stage `n*`.
+    auto step = [&](int idx, uint16_t* nq, uint16_t* ng, float* nl, float* nd, const uint16_t* cq,
+                    const uint16_t* cg, const float* cl, const float* cd) {
+      compute(idx, cq, cg, cl, cd, [&]() {
+        if (idx + 1 < ntiles) issue(idx + 1, nq, ng, nl, nd);
+      });
+      wait_vmem();
+      __syncthreads();
+    };
+
+    if (ntiles > 0) issue(0, q_s0, g_s0, l_s0, d_s0);
+    wait_vmem();
+    __syncthreads();
+    for (int idx = 0; idx < ntiles; idx += 2) {
+      step(idx, q_s1, g_s1, l_s1, d_s1, q_s0, g_s0, l_s0, d_s0);
+      if (idx + 1 >= ntiles) break;
+      step(idx + 1, q_s0, g_s0, l_s0, d_s0, q_s1, g_s1, l_s1, d_s1);
     }
   }
 
@@ -207,8 +271,9 @@ struct DqCfg {
   static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KSTRIDE = D + 8;
-  static constexpr int KTILE = BN * KSTRIDE;
+  static constexpr int KTILE = BN * D;      // K: swizzled (read row-wise and transposed)
+  static constexpr int VSTRIDE = D + 8;     // V: padded (row-wise reads only)
+  static constexpr int VTILE = BN * VSTRIDE;
   static constexpr int CPR = D / 8;
   static constexpr int CPT = BN * CPR / THREADS;
   static_assert(BN * CPR % THREADS == 0, "tile must split evenly");
@@ -217,7 +282,7 @@ struct DqCfg {
 template <int D>
 __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * C::KTILE];  // [buf][K, V]
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::KTILE + C::VTILE)];  // [buf][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -279,14 +344,14 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
     }
   };
   auto lstore = [&](int buf) {
-    uint16_t* kl = lds + buf * 2 * C::KTILE;
+    uint16_t* kl = lds + buf * (C::KTILE + C::VTILE);
     uint16_t* vl = kl + C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int ch = tid + C::THREADS * i;
       const int row = ch / C::CPR, cc = ch % C::CPR;
-      lds_write16(kl + row * C::KSTRIDE + cc * 8, kr[i]);
-      lds_write16(vl + row * C::KSTRIDE + cc * 8, vr[i]);
+      lds_write16(kl + swz_off<D>(row, cc * 8), kr[i]);
+      lds_write16(vl + row * C::VSTRIDE + cc * 8, vr[i]);
     }
   };
 
@@ -303,7 +368,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   for (int it = 0; it < ntiles; ++it) {
     const int k0 = it * C::BN;
     if (it + 1 < ntiles) gload(k0 + C::BN);
-    const uint16_t* kl = lds + (it & 1) * 2 * C::KTILE;
+    const uint16_t* kl = lds + (it & 1) * (C::KTILE + C::VTILE);
     const uint16_t* vl = kl + C::KTILE;
 
     // S^T = K Q^T and dP^T = V dO^T: lane = query row, registers = keys.
@@ -312,9 +377,8 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
     for (int t = 0; t < C::KS; ++t)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int off = (32 * j + l32) * C::KSTRIDE + 16 * t + 8 * hh;
-        s[j] = mfma_bf16(lds_read16(kl + off), qf[t], s[j]);
-        dp[j] = mfma_bf16(lds_read16(vl + off), gf[t], dp[j]);
+        s[j] = mfma_bf16(lds_read16(kl + swz_off<D>(32 * j + l32, 16 * t + 8 * hh)), qf[t], s[j]);
+        dp[j] = mfma_bf16(lds_read16(vl + (32 * j + l32) * C::VSTRIDE + 16 * t + 8 * hh), gf[t], dp[j]);
       }
 
     const bool need_mask = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
@@ -342,11 +406,10 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
     // dQ^T += K^T dS^T (k = keys).
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint16_t* krow = kl + (16 * ks + tr_row) * C::KSTRIDE + tr_col;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const u32x2_t lo = lds_read_tr(krow + 32 * db);
-        const u32x2_t hi = lds_read_tr(krow + 8 * C::KSTRIDE + 32 * db);
+        const u32x2_t lo = lds_read_tr(kl + swz_off<D>(16 * ks + tr_row, 32 * db + tr_col));
+        const u32x2_t hi = lds_read_tr(kl + swz_off<D>(16 * ks + tr_row + 8, 32 * db + tr_col));
         acc[db] = mfma_bf16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, dsb[ks], acc[db]);
       }
     }
@@ -374,7 +437,8 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
     launch_delta_any(a, D, true, s);
   } else if (pass == kBwdDkdv) {
     const long kblocks = (long)a.num_ktiles * a.Hkv * a.B;
-    if (kblocks > 0) hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(256), 0, s, a);
+    if (kblocks > 0)
+      hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(DkvCfg<D>::THREADS), 0, s, a);
   } else {
     const long nqt = (a.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
     const long qblocks = nqt * a.Hq * a.B;

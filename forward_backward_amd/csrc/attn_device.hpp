@@ -69,6 +69,70 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// LDS bank model used for layouts (measured with the bank-conflict counter):
+// 64 banks of 4 bytes; a 128-bit read serves 16 lanes per cycle, the 64-bit
+// transpose read 32 lanes per cycle.
+//
+// Tiles read both row-wise (16-byte chunks, 16 consecutive rows per cycle)
+// and with the transpose read (4 consecutive rows x 64 bytes per cycle) use
+// an unpadded row stride of D elements and store logical 16-byte chunk c of
+// row r at physical chunk c ^ swz_f(r). swz_f takes 16 (D=128) or 8 (D=64,
+// two rows per bank line) distinct values over consecutive rows, and gives
+// the 4 rows of a transpose read disjoint groups of 4 chunks.
+template <int D>
+__device__ __forceinline__ int swz_f(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+
+// Element offset of logical (row, col) in a swizzled tile; col % 4 == 0.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz_f<D>(r))) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Asynchronous global -> LDS copy of rows [r0, r0 + ROWS) of a bf16 matrix
+// with row stride `rs` elements into a swizzled [ROWS, D] LDS tile, by the
+// THREADS threads of the workgroup. global_load_lds_dwordx4 writes lane i's
+// 16 bytes to LDS base + 16 * i; the swizzle is realised by choosing which
+// logical chunk each lane fetches. Rows at or past `rlim` (>= 1) re-read row
+// rlim - 1: the caller masks their contribution, and nothing outside the
+// valid rows is ever read. Completion: s_waitcnt vmcnt(0) then a barrier.
+template <int D, int ROWS, int THREADS>
+__device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long rs, int r0, int rlim, int tid) {
+  constexpr int RPW = 1024 / (2 * D);  // rows per wave per instruction
+  constexpr int CPR = D / 8;
+  constexpr int WAVES = THREADS / 64;
+  constexpr int ITERS = ROWS / (RPW * WAVES);
+  static_assert(ROWS % (RPW * WAVES) == 0, "tile rows must split evenly over the waves");
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    const int wi = i * WAVES + wave;
+    const int r = wi * RPW + lane / CPR;
+    const int c = (lane % CPR) ^ swz_f<D>(r);
+    int gr = r0 + r;
+    gr = gr < rlim ? gr : rlim - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(g + gr * rs + c * 8), (lds_void_t*)(tile + wi * 512), 16, 0, 0);
+  }
+}
+
+// Asynchronous copy of 64 consecutive floats (indices clamped to < lim, lim >= 1)
+// into LDS by one wave.
+__device__ __forceinline__ void dma_row64(float* dst, const float* g, int i0, int lim, int lane) {
+  int i = i0 + lane;
+  i = i < lim ? i : lim - 1;
+  __builtin_amdgcn_global_load_lds((const void*)(g + i), (lds_void_t*)dst, 4, 0, 0);
+}
+
+// Wait for this wave's outstanding global loads (including LDS DMA).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Workgroups are dispatched round-robin over the 8 XCDs of the chip; map the
 // hardware id to a logical id so that each XCD gets a contiguous range of
 // logical ids (neighbouring tiles of one head then share that XCD's L2).

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(64) void attn_dkdv_fp32_kernel(BwdArgs a) {
   }
 }
 
-// D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32.
+// D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32, and the
+// base-2 LSE (LSE * log2(e)) that the tile kernels load straight into LDS.
 // Each thread reduces 8 contiguous elements; D/8 threads share a row.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void attn_delta_kernel(BwdArgs a, long rows) {
@@ -202,7 +203,9 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(BwdArgs a, long rows) {
     const int h = (int)(row % a.Hq);
     const int i = (int)((row / a.Hq) % a.Tq);
     const int b = (int)(row / ((long)a.Hq * a.Tq));
-    a.delta[((long)b * a.Hq + h) * a.Tq + i] = acc;
+    const long st = ((long)b * a.Hq + h) * a.Tq + i;
+    a.delta[st] = acc;
+    a.lse2[st] = a.lse[st] * 1.4426950408889634f;
   }
 }
 

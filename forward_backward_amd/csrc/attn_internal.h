@@ -34,6 +34,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;            // workspace: D = rowsum(dO * O), [B, Hq, Tq]
+  float* lse2;             // workspace: LSE * log2(e), [B, Hq, Tq]
   const int32_t* kv_lens;
   int B, Tq, Tkv, Hq, Hkv;
   float scale;

@@ -80,7 +80,8 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op);
 attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o,
                        float* lse, void* stream);
 
-/* Bytes of device workspace attn_bwd needs (fp32 D = rowsum(dO * O)). */
+/* Bytes of device workspace attn_bwd needs: two fp32 [B, Hq, Tq] row
+ * statistics, D = rowsum(dO * O) and LSE * log2(e). */
 size_t attn_bwd_workspace_size(const attn_params_t* p);
 
 /* Backward: deterministic two-pass scheme without atomics. A pre-kernel
@@ -95,12 +96,12 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        size_t workspace_bytes, void* stream);
 
 /* The three passes of attn_bwd as separate calls, in the order attn_bwd
- * runs them. attn_bwd_preprocess writes D = rowsum(dO * O) into the
- * workspace; attn_bwd_dkdv and attn_bwd_dq read it and are independent of
- * each other, so a caller may run them on two streams once the
- * preprocess has completed. Arguments mean what they mean for attn_bwd. */
-attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const void* dout, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+ * runs them. attn_bwd_preprocess writes D = rowsum(dO * O) and LSE * log2(e)
+ * into the workspace; attn_bwd_dkdv and attn_bwd_dq read them and are
+ * independent of each other, so a caller may run them on two streams once
+ * the preprocess has completed. Arguments mean what they mean for attn_bwd. */
+attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const float* lse, const void* dout,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
                             const void* dout, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
                             void* stream);

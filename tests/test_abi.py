@@ -85,12 +85,12 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.attn_fwd(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == attn.ATTN_ERR_INVALID
     args = [FAKE] * 9
     need = L.attn_bwd_workspace_size(ctypes.byref(p))
-    assert need == 2 * 8 * 128 * 4
+    assert need == 2 * (2 * 8 * 128 * 4)
     assert L.attn_bwd(ctypes.byref(p), *args, None, 0, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), *args, FAKE, need - 1, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), None, *args[1:], FAKE, need, None) == attn.ATTN_ERR_INVALID
-    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, need - 1, None) == attn.ATTN_ERR_WORKSPACE
-    assert L.attn_bwd_preprocess(ctypes.byref(p), None, FAKE, FAKE, need, None) == attn.ATTN_ERR_INVALID
+    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, need - 1, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_bwd_preprocess(ctypes.byref(p), FAKE, None, FAKE, FAKE, need, None) == attn.ATTN_ERR_INVALID
     assert L.attn_bwd_dkdv(ctypes.byref(p), *([FAKE] * 7), None, 0, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd_dkdv(ctypes.byref(p), *([FAKE] * 6), None, FAKE, need, None) == attn.ATTN_ERR_INVALID
     assert L.attn_bwd_dq(ctypes.byref(p), *([FAKE] * 6), FAKE, need - 4, None) == attn.ATTN_ERR_WORKSPACE
