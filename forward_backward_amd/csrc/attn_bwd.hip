@@ -267,22 +267,23 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
 template <int D>
 struct DqCfg {
   static constexpr int BM = 128;            // query rows, 32 per wave
-  static constexpr int BN = 64;             // keys per tile
+  static constexpr int BN = 64;             // keys per tile (2 blocks of 32)
   static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KTILE = BN * D;      // K: swizzled (read row-wise and transposed)
-  static constexpr int VSTRIDE = D + 8;     // V: padded (row-wise reads only)
-  static constexpr int VTILE = BN * VSTRIDE;
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = BN * CPR / THREADS;
-  static_assert(BN * CPR % THREADS == 0, "tile must split evenly");
+  static constexpr int TILE = BN * D;       // K and V tiles: swizzled, unpadded
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   using C = DqCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::KTILE + C::VTILE)];  // [buf][K, V]
+  // Two pipeline stages of the K and V tiles in one array (one per-lane
+  // offset plus a constant addresses every stage).
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * C::TILE];
+  uint16_t* const k_s0 = tiles;
+  uint16_t* const v_s0 = tiles + C::TILE;
+  uint16_t* const k_s1 = tiles + 2 * C::TILE;
+  uint16_t* const v_s1 = tiles + 3 * C::TILE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
     gf[t] = row_ok ? gload16((const uint16_t*)a.dout + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
   }
   const long stat = ((long)b * a.Hq + h) * a.Tq + qrow;
-  const float lse2 = row_ok ? a.lse[stat] * kLog2e : INFINITY;
+  const float lse2 = row_ok ? a.lse2[stat] : INFINITY;
   const float dlt = row_ok ? a.delta[stat] : 0.f;
   const float c = a.scale_log2;
 
@@ -327,95 +328,103 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) acc[i] = f32x16_t{};
 
-  u32x4_t kr[C::CPT], vr[C::CPT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + C::THREADS * i;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      const int kk = k0 + row;
-      if (kk < kv_end) {
-        kr[i] = gload16(kb + kk * krs + cc * 8);
-        vr[i] = gload16(vb + kk * krs + cc * 8);
-      } else {
-        kr[i] = u32x4_t{0, 0, 0, 0};
-        vr[i] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* kl = lds + buf * (C::KTILE + C::VTILE);
-    uint16_t* vl = kl + C::KTILE;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + C::THREADS * i;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      lds_write16(kl + swz_off<D>(row, cc * 8), kr[i]);
-      lds_write16(vl + row * C::VSTRIDE + cc * 8, vr[i]);
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int wave_min_row = q0 + 32 * wave;
+  int nrm[C::KS], trd[C::DB][2];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    trd[db][0] = swz_off<D>(tr_row, 32 * db + tr_col);
+    trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col);
+  }
 
-  for (int it = 0; it < ntiles; ++it) {
+  auto issue = [&](int it, uint16_t* ks, uint16_t* vs) {
     const int k0 = it * C::BN;
-    if (it + 1 < ntiles) gload(k0 + C::BN);
-    const uint16_t* kl = lds + (it & 1) * (C::KTILE + C::VTILE);
-    const uint16_t* vl = kl + C::KTILE;
+    dma_tile<D, C::BN, C::THREADS>(ks, kb, krs, k0, kv_end, tid);
+    dma_tile<D, C::BN, C::THREADS>(vs, vb, krs, k0, kv_end, tid);
+  };
 
-    // S^T = K Q^T and dP^T = V dO^T: lane = query row, registers = keys.
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+  auto compute = [&](int it, const uint16_t* kl, const uint16_t* vl, auto&& issue_next) {
+    const int k0 = it * C::BN;
 #pragma unroll
-    for (int t = 0; t < C::KS; ++t)
+    for (int j = 0; j < 2; ++j) {
+      const uint16_t* krow = kl + 32 * j * D;
+      const uint16_t* vrow = vl + 32 * j * D;
+      u32x4_t ka[C::KS], va[C::KS];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        s[j] = mfma_bf16(lds_read16(kl + swz_off<D>(32 * j + l32, 16 * t + 8 * hh)), qf[t], s[j]);
-        dp[j] = mfma_bf16(lds_read16(vl + (32 * j + l32) * C::VSTRIDE + 16 * t + 8 * hh), gf[t], dp[j]);
+      for (int t = 0; t < C::KS; ++t) {
+        ka[t] = lds_read16(krow + nrm[t]);
+        va[t] = lds_read16(vrow + nrm[t]);
       }
-
-    const bool need_mask = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
-    u32x4_t dsb[4];
+      __builtin_amdgcn_sched_barrier(0);
+      // S^T = K Q^T and dP^T = V dO^T: lane = query row, registers = keys.
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int t = 0; t < C::KS; ++t) {
+        s = mfma_bf16(ka[t], qf[t], s);
+        dp = mfma_bf16(va[t], gf[t], dp);
+      }
+      // Transposed K fragments for dQ^T += K^T dS^T, requested while S and dP run.
+      u32x2_t kt[2][C::DB][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint16_t* kblk = kl + (32 * j + 16 * u) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          kt[u][db][0] = lds_read_tr(kblk + trd[db][0]);
+          kt[u][db][1] = lds_read_tr(kblk + trd[db][1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // The next tile's loads start after the first block's transpose reads
+      // (transpose reads issued while they are in flight wait for them).
+      if (j == 0) issue_next();
+      const int kblk0 = k0 + 32 * j;
+      const bool need_mask = (kblk0 + 32 > kvlim) || (a.causal && kblk0 + 31 > wave_min_row);
+      u32x4_t dsb[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         float dsv[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int r = 8 * u + x;
-          float p = fast_exp2(__builtin_fmaf(s[j][r], c, -lse2));
+          float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
           if (need_mask) {
-            const int kk = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = kk < kvlim && (!a.causal || kk <= qrow);
+            const int kk = kblk0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = (kk < kvlim) & (!a.causal | (kk <= qrow));
             p = ok ? p : 0.f;
           }
-          dsv[x] = p * (dp[j][r] - dlt);
+          dsv[x] = p * (dp[r] - dlt);
         }
-        dsb[2 * j + u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                                 pack_bf16(dsv[6], dsv[7])};
+        dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                         pack_bf16(dsv[6], dsv[7])};
       }
-
-    // dQ^T += K^T dS^T (k = keys).
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const u32x2_t lo = lds_read_tr(kl + swz_off<D>(16 * ks + tr_row, 32 * db + tr_col));
-        const u32x2_t hi = lds_read_tr(kl + swz_off<D>(16 * ks + tr_row + 8, 32 * db + tr_col));
-        acc[db] = mfma_bf16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, dsb[ks], acc[db]);
-      }
+        for (int db = 0; db < C::DB; ++db)
+          acc[db] = mfma_bf16(u32x4_t{kt[u][db][0][0], kt[u][db][0][1], kt[u][db][1][0], kt[u][db][1][1]}, dsb[u],
+                              acc[db]);
     }
+  };
 
-    if (it + 1 < ntiles) lstore((it + 1) & 1);
+  auto step = [&](int it, uint16_t* nk, uint16_t* nv, const uint16_t* ck, const uint16_t* cv) {
+    compute(it, ck, cv, [&]() {
+      if (it + 1 < ntiles) issue(it + 1, nk, nv);
+    });
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (ntiles > 0) issue(0, k_s0, v_s0);
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, k_s1, v_s1, k_s0, v_s0);
+    if (it + 1 >= ntiles) break;
+    step(it + 1, k_s0, v_s0, k_s1, v_s1);
   }
 
   if (row_ok) {
