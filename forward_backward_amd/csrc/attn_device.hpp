@@ -96,14 +96,57 @@ __device__ __forceinline__ int swz_off(int r, int col) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((const lds_void_t*)p));
+}
+
+// global_load_lds_dword{,x4}: lane i's 4 or 16 bytes land at LDS address
+// m0 + (4 or 16) * i. Issued as inline assembly so that the compiler does not
+// treat the copy as an LDS store that later LDS reads of *other* buffers
+// must wait for; the kernels order the copy themselves: the destination is
+// read only after s_waitcnt vmcnt(0) (wait_vmem) and a workgroup barrier.
+// Loads complete in order, so the compiler's own vmcnt waits for other loads
+// stay correct (they can only wait longer).
+// M0 is saved and restored around the copy (the compiler neither knows nor
+// expects it to change); the LDS address must be wave-uniform and is moved
+// into a scalar register first.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(base)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(base)
+      : "memory");
+}
+
 // Asynchronous global -> LDS copy of rows [r0, r0 + ROWS) of a bf16 matrix
 // with row stride `rs` elements into a swizzled [ROWS, D] LDS tile, by the
-// THREADS threads of the workgroup. global_load_lds_dwordx4 writes lane i's
-// 16 bytes to LDS base + 16 * i; the swizzle is realised by choosing which
-// logical chunk each lane fetches. Rows at or past `rlim` (>= 1) re-read row
-// rlim - 1: the caller masks their contribution, and nothing outside the
-// valid rows is ever read. Completion: s_waitcnt vmcnt(0) then a barrier.
-template <int D, int ROWS, int THREADS>
+// THREADS threads of the workgroup: each wave copies 1 KiB per instruction,
+// and the swizzle is realised by choosing which logical chunk each lane
+// fetches. Rows at or past `rlim` (>= 1) re-read row rlim - 1: the caller
+// masks their contribution, and nothing outside the valid rows is read.
+// VISIBLE = true issues the copy through the compiler builtin instead, so the
+// compiler orders later LDS reads after it itself (it cannot tell stages of
+// one array apart and waits before transpose reads in particular).
+template <int D, int ROWS, int THREADS, bool VISIBLE = false>
 __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long rs, int r0, int rlim, int tid) {
   constexpr int RPW = 1024 / (2 * D);  // rows per wave per instruction
   constexpr int CPR = D / 8;
@@ -118,7 +161,10 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long
     const int c = (lane % CPR) ^ swz_f<D>(r);
     int gr = r0 + r;
     gr = gr < rlim ? gr : rlim - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(g + gr * rs + c * 8), (lds_void_t*)(tile + wi * 512), 16, 0, 0);
+    if constexpr (VISIBLE)
+      __builtin_amdgcn_global_load_lds((const void*)(g + gr * rs + c * 8), (lds_void_t*)(tile + wi * 512), 16, 0, 0);
+    else
+      dma16(g + gr * rs + c * 8, lds_addr(tile + wi * 512));
   }
 }
 
@@ -127,7 +173,7 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long
 __device__ __forceinline__ void dma_row64(float* dst, const float* g, int i0, int lim, int lane) {
   int i = i0 + lane;
   i = i < lim ? i : lim - 1;
-  __builtin_amdgcn_global_load_lds((const void*)(g + i), (lds_void_t*)dst, 4, 0, 0);
+  dma4(g + i, lds_addr(dst));
 }
 
 // Wait for this wave's outstanding global loads (including LDS DMA).
