@@ -42,6 +42,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SYMBOLS = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_preprocess": "attn_delta_kernel",
+                  "bwd_dkdv": "attn_dkdv_bf16_kernel", "bwd_dq": "attn_dq_bf16_kernel",
+                  "decode_split": "attn_decode_split_kernel", "decode_combine": "attn_decode_combine_kernel"}
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -53,6 +58,11 @@ def parse_args():
     ap.add_argument("--decode-calls", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of this many MiB (reference dispatch for HBM counters)")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="turn rocprofv3 CSV output (kernel-trace stats, FETCH_SIZE pass, WRITE_SIZE pass) into "
+                         "the summaries under profiles/ and exit (no GPU use)")
+    ap.add_argument("--profile-command", default="", help="kernel-trace command recorded in the summaries")
+    ap.add_argument("--counter-command", default="", help="counter-pass command recorded in the summaries")
     return ap.parse_args()
 
 
@@ -79,6 +89,118 @@ def stored_traffic(kernel: str):
     if not entry or rec.get("source_digest") != source_digest():
         return None
     return entry.get("bytes_per_launch")
+
+
+def _short_name(kernel_name):
+    import re
+    k = kernel_name.replace("void ", "").replace("attn::(anonymous namespace)::", "")
+    return re.sub(r"\(.*", "", k)
+
+
+def _read_counter_csv(directory, counter):
+    """Per-kernel list of per-dispatch values of `counter` from a rocprofv3 --pmc CSV."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (_short_name(r["Kernel_Name"]), int(r["Dispatch_Id"]), r["Grid_Size"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (name, _, grid), v in per.items():
+            out.setdefault((name, grid), []).append(v)
+    return out
+
+
+def summarize(stats_dir, fetch_dir, write_dir, command, counter_command):
+    """Write profiles/ summaries from rocprofv3 output (runs on any host)."""
+    import csv
+    import glob
+
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    rows = []
+    for path in glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            rows.append((_short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]), float(r["TotalDurationNs"]),
+                         float(r["MinNs"]), float(r["MaxNs"])))
+    rows.sort(key=lambda x: -x[3])
+    lines = ["# Kernel durations: attention fwd+bwd B4 H8 d128 T8192 (+ causal and GQA decode legs)", "",
+             "Produced by:", "", "```", command or "(command not recorded)", "```", "",
+             "| kernel | calls | average us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, tot, mn, mx in rows:
+        if not name.startswith("attn"):
+            continue
+        lines.append(f"| `{name}` | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | {tot / 1e6:.3f} |")
+    # Per-leg averages from the dispatch trace: bench.py runs the non-causal
+    # headline leg first (warmup + steps dispatches of each kernel), then the
+    # causal leg (1 warmup + steps).
+    import re as _re
+    w = int((_re.search(r"--warmup (\d+)", command or "") or [None, 3])[1])
+    k = int((_re.search(r"--steps (\d+)", command or "") or [None, 20])[1])
+    per_kernel = {}
+    for path in glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            name = _short_name(r["Kernel_Name"])
+            if name.startswith("attn"):
+                per_kernel.setdefault(name, []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    lines += ["", "Per leg, from the dispatch trace (the headline non-causal leg runs first: "
+              f"{w} warmup + {k} timed steps; then the causal leg):", "",
+              "| kernel | headline leg: dispatches | headline leg: average us (timed steps) | causal leg: average us |",
+              "|---|---|---|---|"]
+    for name, ds in sorted(per_kernel.items()):
+        ds.sort()
+        if name.startswith("attn_decode"):
+            continue
+        head = [d for _, d in ds[:w + k]]
+        timed = head[w:] if len(head) > w else head
+        rest = [d for _, d in ds[w + k:w + k + 1 + k]][1:]
+        lines.append(f"| `{name}` | {len(head)} | {sum(timed) / max(len(timed), 1) / 1e3:.2f} | "
+                     f"{(sum(rest) / len(rest) / 1e3) if rest else float('nan'):.2f} |")
+    with open(os.path.join(prof, "fwd_bwd_d128_T8192_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch = _read_counter_csv(fetch_dir, "FETCH_SIZE")
+    write = _read_counter_csv(write_dir, "WRITE_SIZE")
+    copy_f = [v for (n, g), vs in fetch.items() if "copyBuffer" in n for v in vs]
+    copy_w = [v for (n, g), vs in write.items() if "copyBuffer" in n for v in vs]
+    copy_kib = None
+    # The calibration dispatch is the largest plain copy in the run.
+    if copy_w:
+        copy_kib = max(copy_w)
+    f_factor = copy_kib / max(copy_f) if copy_f and copy_kib else None
+    w_factor = 1.0 if copy_kib else None
+    lines = ["# HBM traffic per dispatch: attention fwd+bwd B4 H8 d128 T8192, non-causal", "",
+             "Two rocprofv3 counter passes of the command below, one with FETCH_SIZE, one with WRITE_SIZE (KiB "
+             "per dispatch), each scaled by what the counter reads for a plain device copy of known size run in "
+             "the same process (`--copy-calibration 256`: 256 MiB read, 256 MiB written).", "",
+             "```", counter_command or "", "```", "",
+             f"Copy calibration: WRITE_SIZE {copy_kib} KiB for 262144 KiB written (factor {w_factor}); "
+             f"FETCH_SIZE {max(copy_f) if copy_f else None} KiB for 262144 KiB read (factor {f_factor}).", "",
+             "| kernel | grid | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM MiB per launch |", "|---|---|---|---|---|"]
+    traffic = {}
+    for (name, grid), fv in sorted(fetch.items()):
+        if not name.startswith("attn"):
+            continue
+        wv = write.get((name, grid), [0.0])
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        total = None
+        if f_factor:
+            total = (fk * f_factor + wk * w_factor) * 1024
+            base = name.split("<")[0]
+            if base not in traffic or total > traffic[base]:
+                traffic[base] = total
+        lines.append(f"| `{name}` | {grid} | {fk:.0f} | {wk:.0f} | "
+                     f"{'' if total is None else f'{total / 2**20:.1f}'} |")
+    with open(os.path.join(prof, "fwd_bwd_d128_T8192_hbm_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(prof, "hbm_traffic.json"), "w") as f:
+        json.dump({"source_digest": source_digest(), "command": counter_command,
+                   "kernels": {k: {"bytes_per_launch": round(v)} for k, v in traffic.items()}}, f, indent=1)
+    print(f"wrote summaries under {prof}")
 
 
 def device_tensors(case, seed=0, with_do=True):
@@ -208,6 +330,9 @@ def cpu_baseline(case, seconds):
 
 def main():
     args = parse_args()
+    if args.summarize:
+        summarize(*args.summarize, args.profile_command, args.counter_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
@@ -245,8 +370,7 @@ def main():
 
     fwd_f = attention_flops(full.B, full.Hq, full.Tq, full.Tkv, full.D, False, "fwd")
     kernel_flops = {"attn_fwd": fwd_f, "bwd_dkdv": 2 * fwd_f, "bwd_dq": 1.5 * fwd_f}
-    kernel_symbol = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_dkdv": "attn_dkdv_bf16_kernel",
-                     "bwd_dq": "attn_dq_bf16_kernel"}
+    kernel_symbol = KERNEL_SYMBOLS
     dom = max(kernel_flops, key=lambda n: per[n])
     achieved = kernel_flops[dom] / (per[dom] * 1e-3) / 1e12
     roofline = {
