@@ -17,6 +17,8 @@
 // is arranged so the register layouts line up (see attn_device.hpp), and the
 // transposed operand (dO^T, Q^T, K^T) is read with the LDS transpose read.
 // KV tiles wholly past kv_len store zeros without running their loop.
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
@@ -357,68 +359,99 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
     dma_tile<D, C::BN, C::THREADS, true>(vs, vb, krs, k0, kv_end, tid);
   };
 
+  // Row fragments of key block j (32 keys) for S^T = K Q^T and dP^T = V dO^T.
+  auto read_kv = [&](const uint16_t* kl, const uint16_t* vl, int j, u32x4_t* ka, u32x4_t* va) {
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) {
+      ka[t] = lds_read16(kl + 32 * j * D + nrm[t]);
+      va[t] = lds_read16(vl + 32 * j * D + nrm[t]);
+    }
+  };
+  // Transposed K fragments of key block j for dQ^T += K^T dS^T.
+  auto read_kt = [&](const uint16_t* kl, int j, u32x2_t (*kt)[C::DB][2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        kt[u][db][0] = lds_read_tr(kl + (32 * j + 16 * u) * D + trd[db][0]);
+        kt[u][db][1] = lds_read_tr(kl + (32 * j + 16 * u) * D + trd[db][1]);
+      }
+  };
+  auto sdp = [&](const u32x4_t* ka, const u32x4_t* va, f32x16_t& s, f32x16_t& dp) {
+    s = f32x16_t{};
+    dp = f32x16_t{};
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) {
+      s = mfma_bf16(ka[t], qf[t], s);
+      dp = mfma_bf16(va[t], gf[t], dp);
+    }
+  };
+  // dS^T of key block j as bf16 B operands; MASK selects the element-wise mask.
+  auto softmax = [&](auto mask_tag, int kblk0, const f32x16_t& s, const f32x16_t& dp, u32x4_t* dsb) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float dsv[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int r = 8 * u + x;
+        float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+        if constexpr (MASK) {
+          const int kk = kblk0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool ok = (kk < kvlim) & (!a.causal | (kk <= qrow));
+          p = ok ? p : 0.f;
+        }
+        dsv[x] = p * (dp[r] - dlt);
+      }
+      dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                       pack_bf16(dsv[6], dsv[7])};
+    }
+  };
+  auto dq_mfma = [&](u32x2_t (*kt)[C::DB][2], const u32x4_t* dsb) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        acc[db] = mfma_bf16(u32x4_t{kt[u][db][0][0], kt[u][db][0][1], kt[u][db][1][0], kt[u][db][1][1]}, dsb[u],
+                            acc[db]);
+  };
+
+  // One 64-key tile as a two-block software pipeline: the S/dP products of
+  // block 1 are interleaved with the softmax of block 0, so that the vector
+  // work runs while the matrix core is busy.
   auto compute = [&](int it, const uint16_t* kl, const uint16_t* vl, auto&& issue_next) {
     const int k0 = it * C::BN;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint16_t* krow = kl + 32 * j * D;
-      const uint16_t* vrow = vl + 32 * j * D;
+    const bool mask_tile = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
+    auto body = [&](auto mask_tag) {
       u32x4_t ka[C::KS], va[C::KS];
-#pragma unroll
-      for (int t = 0; t < C::KS; ++t) {
-        ka[t] = lds_read16(krow + nrm[t]);
-        va[t] = lds_read16(vrow + nrm[t]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // S^T = K Q^T and dP^T = V dO^T: lane = query row, registers = keys.
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-      for (int t = 0; t < C::KS; ++t) {
-        s = mfma_bf16(ka[t], qf[t], s);
-        dp = mfma_bf16(va[t], gf[t], dp);
-      }
-      // Transposed K fragments for dQ^T += K^T dS^T, requested while S and dP run.
+      f32x16_t s0, dp0, s1, dp1;
       u32x2_t kt[2][C::DB][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint16_t* kblk = kl + (32 * j + 16 * u) * D;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          kt[u][db][0] = lds_read_tr(kblk + trd[db][0]);
-          kt[u][db][1] = lds_read_tr(kblk + trd[db][1]);
-        }
-      }
+      u32x4_t dsb[2];
+      read_kv(kl, vl, 0, ka, va);
+      sdp(ka, va, s0, dp0);
+      read_kv(kl, vl, 1, ka, va);
+      read_kt(kl, 0, kt);
       __builtin_amdgcn_sched_barrier(0);
       // The next tile's loads start after the first block's transpose reads
       // (transpose reads issued while they are in flight wait for them).
-      if (j == 0) issue_next();
-      const int kblk0 = k0 + 32 * j;
-      const bool need_mask = (kblk0 + 32 > kvlim) || (a.causal && kblk0 + 31 > wave_min_row);
-      u32x4_t dsb[2];
+      issue_next();
+      sdp(ka, va, s1, dp1);
+      softmax(mask_tag, k0, s0, dp0, dsb);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float dsv[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int r = 8 * u + x;
-          float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
-          if (need_mask) {
-            const int kk = kblk0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = (kk < kvlim) & (!a.causal | (kk <= qrow));
-            p = ok ? p : 0.f;
-          }
-          dsv[x] = p * (dp[r] - dlt);
-        }
-        dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                         pack_bf16(dsv[6], dsv[7])};
+      for (int i = 0; i < 2 * C::KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then vector ALU work
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          acc[db] = mfma_bf16(u32x4_t{kt[u][db][0][0], kt[u][db][0][1], kt[u][db][1][0], kt[u][db][1][1]}, dsb[u],
-                              acc[db]);
-    }
+      __builtin_amdgcn_sched_barrier(0);
+      dq_mfma(kt, dsb);
+      read_kt(kl, 1, kt);
+      softmax(mask_tag, k0 + 32, s1, dp1, dsb);
+      dq_mfma(kt, dsb);
+    };
+    if (mask_tile)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
   };
 
   auto step = [&](int it, uint16_t* nk, uint16_t* nv, const uint16_t* ck, const uint16_t* cv) {
