@@ -31,43 +31,34 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ----------------------------------------------------------------- dK / dV
 //
-// Eight waves, two roles, for one 128-key tile (32 keys per wave of each
-// role) and a stream of 64-row query tiles:
-//   P-waves  (0-3): phase 1  S = Q K^T, P = exp2(S*c - LSE2) (masked), P kept
-//                            as bf16 and also stored (fp32) to LDS;
-//                   phase 2  dV^T += dO^T P.
-//   dS-waves (4-7): phase 1  dP = dO V^T;
-//                   phase 2  dS = P (dP - D) with P read from LDS,
-//                            dK^T += Q^T dS.
-// Each product is formed once (16 MFMAs per 32x32 block for each role) and
-// every SIMD runs one wave of each role, so the vector work of one overlaps
-// the matrix work of the other. Two workgroup barriers per query tile.
+// One workgroup per (batch, KV head, 128 keys), 4 waves of 32 keys; K and V
+// rows of the wave's keys stay in registers as B operands. For each query
+// head of the group and each 64-row query tile, in a fixed order:
+//   S = Q K^T, dP = dO V^T       (lane = key, registers = query rows)
+//   P = exp2(S*c - LSE2), dS = P (dP - D)
+//   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T by transpose reads)
+// The tile is a two-block software pipeline: block 1's S/dP products are
+// interleaved with block 0's softmax, so the vector work runs under the
+// matrix work.
 
 template <int D>
 struct DkvCfg {
-  static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave of each role
+  static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave
   static constexpr int BM = 64;             // query rows per LDS tile (2 blocks of 32)
-  static constexpr int NB = BM / 32;
-  static constexpr int THREADS = 512;
+  static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int TILE = BM * D;       // swizzled, unpadded (read row-wise and transposed)
-  // fp32 P handed from P-wave w to dS-wave w + 4: per (wave, block) 16 values
-  // per lane, stored as 4 chunks of 4 floats with the lane index fastest.
-  static constexpr int PBLK = 4 * 64 * 4;
 };
 
 template <int D>
-__global__ __launch_bounds__(512) void attn_dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   using C = DkvCfg<D>;
   // Two pipeline stages of the Q and dO tiles in one array, so that one
   // per-lane offset plus a constant addresses every stage.
   __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * C::TILE];
-  // Row statistics: one array per stage (small), so that reads of the
-  // current stage are not made to wait for the loads into the next one.
   __shared__ __attribute__((aligned(16))) float l_s0[C::BM], l_s1[C::BM];  // LSE * log2(e)
   __shared__ __attribute__((aligned(16))) float d_s0[C::BM], d_s1[C::BM];  // D = rowsum(dO * O)
-  __shared__ __attribute__((aligned(16))) float pbuf[4 * C::NB * C::PBLK];
   uint16_t* const q_s0 = tiles;
   uint16_t* const g_s0 = tiles + C::TILE;   // dO tiles
   uint16_t* const q_s1 = tiles + 2 * C::TILE;
@@ -76,8 +67,6 @@ __global__ __launch_bounds__(512) void attn_dkdv_bf16_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool role_ds = wave >= 4;
-  const int kw = wave & 3;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -88,31 +77,33 @@ __global__ __launch_bounds__(512) void attn_dkdv_bf16_kernel(BwdArgs a) {
   const int b = bkh / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int k0 = kt * C::BN;
-  const int key = k0 + 32 * kw + l32;        // this lane's key
+  const int key = k0 + 32 * wave + l32;      // this lane's key
 
   const long krs = (long)a.Hkv * D;
   const long qrs = (long)a.Hq * D;
   const long kvoff = ((long)b * a.Tkv * a.Hkv + kh) * D;
   const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
-  float* const pw = pbuf + kw * C::NB * C::PBLK;  // this key block's P hand-off area
 
-  f32x16_t acc[C::DB];  // dV (P-waves) or dK (dS-waves)
+  f32x16_t dk[C::DB], dv[C::DB];
 #pragma unroll
-  for (int i = 0; i < C::DB; ++i) acc[i] = f32x16_t{};
+  for (int i = 0; i < C::DB; ++i) {
+    dk[i] = f32x16_t{};
+    dv[i] = f32x16_t{};
+  }
 
   if (k0 < kvlim) {
-    // K rows (P-waves) or V rows (dS-waves) of this lane's key as B operands.
-    u32x4_t bf[C::KS];
-    {
-      const bool key_ok = key < kvlim;
-      const uint16_t* src = (const uint16_t*)(role_ds ? a.v : a.k) + kvoff + key * krs;
+    // K and V rows of this lane's key as B operands (k = head_dim).
+    u32x4_t kf[C::KS], vf[C::KS];
+    const bool key_ok = key < kvlim;
 #pragma unroll
-      for (int t = 0; t < C::KS; ++t) bf[t] = key_ok ? gload16(src + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    for (int t = 0; t < C::KS; ++t) {
+      kf[t] = key_ok ? gload16((const uint16_t*)a.k + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+      vf[t] = key_ok ? gload16((const uint16_t*)a.v + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
     }
     const float c = a.scale_log2;
     const int tr_row = 4 * hh + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int wave_min_key = k0 + 32 * kw;
+    const int wave_min_key = k0 + 32 * wave;
     const int wave_max_key = wave_min_key + 31;
     const int qt_begin = a.causal ? k0 / C::BM : 0;
     const int nqt = (a.Tq + C::BM - 1) / C::BM;
@@ -141,107 +132,109 @@ __global__ __launch_bounds__(512) void attn_dkdv_bf16_kernel(BwdArgs a) {
       if (wave == 1) dma_row64(ds, a.delta + stat0, q0, a.Tq, lane);
     };
 
-    // A block is skipped when every query row precedes every key of the wave
-    // (causal) or lies past Tq; both roles of a key block agree on it.
-    auto active = [&](int q0, int qb) {
-      const int qmin = q0 + 32 * qb;
-      return qmin < a.Tq && !(a.causal && qmin + 31 < wave_min_key);
+    auto read_qg = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, u32x4_t* qa, u32x4_t* ga) {
+#pragma unroll
+      for (int t = 0; t < C::KS; ++t) {
+        qa[t] = lds_read16(qsb + 32 * qb * D + nrm[t]);
+        ga[t] = lds_read16(gsb + 32 * qb * D + nrm[t]);
+      }
+    };
+    auto sdp = [&](const u32x4_t* qa, const u32x4_t* ga, f32x16_t& s, f32x16_t& dp) {
+      s = f32x16_t{};
+      dp = f32x16_t{};
+#pragma unroll
+      for (int t = 0; t < C::KS; ++t) {
+        s = mfma_bf16(qa[t], kf[t], s);
+        dp = mfma_bf16(ga[t], vf[t], dp);
+      }
+    };
+    // P and dS of block qb as bf16 B operands (16 query rows each).
+    auto softmax = [&](auto mask_tag, const float* ls, const float* ds, int q0, int qb, const f32x16_t& s,
+                       const f32x16_t& dp, u32x4_t* pb, u32x4_t* dsb) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x4_t lv[4], dl[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lv[g] = *(const f32x4_t*)(ls + 32 * qb + 8 * g + 4 * hh);
+        dl[g] = *(const f32x4_t*)(ds + 32 * qb + 8 * g + 4 * hh);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int r = 8 * u + x;
+          float p = fast_exp2(__builtin_fmaf(s[r], c, -lv[r >> 2][r & 3]));
+          if constexpr (MASK) {
+            const int ql = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = (key < kvlim) & (!a.causal | (key <= ql)) & (ql < a.Tq);
+            p = ok ? p : 0.f;
+          }
+          pv[x] = p;
+          dsv[x] = p * (dp[r] - dl[r >> 2][r & 3]);
+        }
+        pb[u] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                        pack_bf16(pv[6], pv[7])};
+        dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                         pack_bf16(dsv[6], dsv[7])};
+      }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS for block qb (transpose reads, then products).
+    auto dvdk = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, const u32x4_t* pb, const u32x4_t* dsb) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint16_t* gblk = gsb + (32 * qb + 16 * u) * D;
+        const uint16_t* qblk = qsb + (32 * qb + 16 * u) * D;
+        u32x2_t gt[C::DB][2], xt[C::DB][2];
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          gt[db][0] = lds_read_tr(gblk + trd[db][0]);
+          gt[db][1] = lds_read_tr(gblk + trd[db][1]);
+          xt[db][0] = lds_read_tr(qblk + trd[db][0]);
+          xt[db][1] = lds_read_tr(qblk + trd[db][1]);
+        }
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          dv[db] = mfma_bf16(u32x4_t{gt[db][0][0], gt[db][0][1], gt[db][1][0], gt[db][1][1]}, pb[u], dv[db]);
+          dk[db] = mfma_bf16(u32x4_t{xt[db][0][0], xt[db][0][1], xt[db][1][0], xt[db][1][1]}, dsb[u], dk[db]);
+        }
+      }
     };
 
-    // One query tile from stage (qsb, gsb, ls, ds); `issue_next` starts the
-    // next tile's loads into the other stage at the top of phase 1, so that
-    // they have all of phase 1 to land before phase 2's transpose reads.
+    // One query tile from stage (qsb, gsb, ls, ds); the next tile's loads into
+    // the other stage start at the top.
     auto tile = [&](int idx, const uint16_t* qsb, const uint16_t* gsb, const float* ls, const float* ds,
                     auto&& issue_next) {
       const int q0 = (qt_begin + idx % nq) * C::BM;
       issue_next();
-      // ---- phase 1
-      u32x4_t pb[C::NB][2];     // P-waves: P as bf16 B operands (16 query rows each)
-      f32x16_t dpv[C::NB];      // dS-waves: dP
+      // Blocks wholly before the wave's first key (causal) contribute nothing.
+      const bool skip0 = a.causal && q0 + 31 < wave_min_key;
+      const bool mask_tile =
+          (wave_max_key >= kvlim) || (a.causal && q0 < wave_max_key) || (q0 + C::BM > a.Tq);
+      auto body = [&](auto mask_tag) {
+        u32x4_t qa[C::KS], ga[C::KS];
+        f32x16_t s0, dp0, s1, dp1;
+        u32x4_t pb[2], dsb[2];
+        read_qg(qsb, gsb, 0, qa, ga);
+        sdp(qa, ga, s0, dp0);
+        read_qg(qsb, gsb, 1, qa, ga);
+        __builtin_amdgcn_sched_barrier(0);
+        sdp(qa, ga, s1, dp1);
+        softmax(mask_tag, ls, ds, q0, 0, s0, dp0, pb, dsb);
 #pragma unroll
-      for (int qb = 0; qb < C::NB; ++qb) {
-        if (!active(q0, qb)) continue;
-        const uint16_t* src = (role_ds ? gsb : qsb) + 32 * qb * D;
-        u32x4_t fa[C::KS];
-#pragma unroll
-        for (int t = 0; t < C::KS; ++t) fa[t] = lds_read16(src + nrm[t]);
-        f32x16_t sc = f32x16_t{};
-#pragma unroll
-        for (int t = 0; t < C::KS; ++t) sc = mfma_bf16(fa[t], bf[t], sc);
-        if (role_ds) {
-          dpv[qb] = sc;
-        } else {
-          const int qmin = q0 + 32 * qb;
-          const bool need_mask =
-              (wave_max_key >= kvlim) || (a.causal && qmin < wave_max_key) || (qmin + 31 >= a.Tq);
-          f32x4_t lv[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) lv[g] = *(const f32x4_t*)(ls + 32 * qb + 8 * g + 4 * hh);
-          float pv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ql = 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            float p = fast_exp2(__builtin_fmaf(sc[r], c, -lv[r >> 2][r & 3]));
-            if (need_mask) {
-              const bool ok = (key < kvlim) & (!a.causal | (key <= q0 + ql)) & (q0 + ql < a.Tq);
-              p = ok ? p : 0.f;
-            }
-            pv[r] = p;
-          }
-          float* pdst = pw + qb * C::PBLK;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *(f32x4_t*)(pdst + (i * 64 + lane) * 4) = f32x4_t{pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]};
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            pb[qb][u] = u32x4_t{pack_bf16(pv[8 * u + 0], pv[8 * u + 1]), pack_bf16(pv[8 * u + 2], pv[8 * u + 3]),
-                                pack_bf16(pv[8 * u + 4], pv[8 * u + 5]), pack_bf16(pv[8 * u + 6], pv[8 * u + 7])};
+        for (int i = 0; i < 2 * C::KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then vector ALU work
         }
-      }
-      __syncthreads();
-      // ---- phase 2
-#pragma unroll
-      for (int qb = 0; qb < C::NB; ++qb) {
-        if (!active(q0, qb)) continue;
-        u32x4_t w[2];
-        if (role_ds) {
-          const float* psrc = pw + qb * C::PBLK;
-          f32x4_t pv[4], dl[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = *(const f32x4_t*)(psrc + (i * 64 + lane) * 4);
-            dl[i] = *(const f32x4_t*)(ds + 32 * qb + 8 * i + 4 * hh);
-          }
-          float dsv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dsv[r] = pv[r >> 2][r & 3] * (dpv[qb][r] - dl[r >> 2][r & 3]);
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            w[u] = u32x4_t{pack_bf16(dsv[8 * u + 0], dsv[8 * u + 1]), pack_bf16(dsv[8 * u + 2], dsv[8 * u + 3]),
-                           pack_bf16(dsv[8 * u + 4], dsv[8 * u + 5]), pack_bf16(dsv[8 * u + 6], dsv[8 * u + 7])};
-        } else {
-          w[0] = pb[qb][0];
-          w[1] = pb[qb][1];
-        }
-        // dV^T += dO^T P (P-waves) or dK^T += Q^T dS (dS-waves); k = query rows.
-        const uint16_t* tsrc = role_ds ? qsb : gsb;
-        u32x2_t xt[2][C::DB][2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint16_t* blk = tsrc + (32 * qb + 16 * u) * D;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            xt[u][db][0] = lds_read_tr(blk + trd[db][0]);
-            xt[u][db][1] = lds_read_tr(blk + trd[db][1]);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-            acc[db] = mfma_bf16(u32x4_t{xt[u][db][0][0], xt[u][db][0][1], xt[u][db][1][0], xt[u][db][1][1]}, w[u],
-                                acc[db]);
-      }
+        __builtin_amdgcn_sched_barrier(0);
+        if (!skip0) dvdk(qsb, gsb, 0, pb, dsb);
+        softmax(mask_tag, ls, ds, q0, 1, s1, dp1, pb, dsb);
+        dvdk(qsb, gsb, 1, pb, dsb);
+      };
+      if (mask_tile)
+        body(std::true_type{});
+      else
+        body(std::false_type{});
       wait_vmem();
       __syncthreads();
     };
@@ -262,15 +255,17 @@ __global__ __launch_bounds__(512) void attn_dkdv_bf16_kernel(BwdArgs a) {
 
   // Store: lane = key, register r of block db = head_dim 32*db + 8*(r/4) + 4*hh + r%4.
   if (key < a.Tkv) {
-    uint16_t* dst = (uint16_t*)(role_ds ? a.dk : a.dv) + kvoff + key * krs;
-    const float mul = role_ds ? a.scale : 1.f;
+    uint16_t* dkp = (uint16_t*)a.dk + kvoff + key * krs;
+    uint16_t* dvp = (uint16_t*)a.dv + kvoff + key * krs;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + 8 * g + 4 * hh;
-        *(u32x2_t*)(dst + d) = u32x2_t{pack_bf16(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
-                                       pack_bf16(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+        *(u32x2_t*)(dkp + d) = u32x2_t{pack_bf16(dk[db][4 * g] * a.scale, dk[db][4 * g + 1] * a.scale),
+                                       pack_bf16(dk[db][4 * g + 2] * a.scale, dk[db][4 * g + 3] * a.scale)};
+        *(u32x2_t*)(dvp + d) = u32x2_t{pack_bf16(dv[db][4 * g], dv[db][4 * g + 1]),
+                                       pack_bf16(dv[db][4 * g + 2], dv[db][4 * g + 3])};
       }
   }
 }
