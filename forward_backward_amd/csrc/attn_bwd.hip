@@ -37,14 +37,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 //   S = Q K^T, dP = dO V^T       (lane = key, registers = query rows)
 //   P = exp2(S*c - LSE2), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T by transpose reads)
-// The tile is a two-block software pipeline: block 1's S/dP products are
-// interleaved with block 0's softmax, so the vector work runs under the
-// matrix work.
+// The tile of four 32-row blocks is a software pipeline: block j+1's S/dP
+// products are interleaved with block j's softmax, so the vector work runs
+// under the matrix work.
 
 template <int D>
 struct DkvCfg {
   static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave
-  static constexpr int BM = 64;             // query rows per LDS tile (2 blocks of 32)
+  static constexpr int BM = 64;             // query rows per LDS tile
+  static constexpr int NB = BM / 32;        // 32-row blocks per tile (pipeline depth)
   static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -128,24 +129,32 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
       dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
       dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
       const long stat0 = ((long)b * a.Hq + h) * a.Tq;
+      static_assert(C::BM == 64, "row statistics are copied by two waves of 64 lanes");
       if (wave == 0) dma_row64(ls, a.lse2 + stat0, q0, a.Tq, lane);
       if (wave == 1) dma_row64(ds, a.delta + stat0, q0, a.Tq, lane);
     };
 
-    auto read_qg = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, u32x4_t* qa, u32x4_t* ga) {
-#pragma unroll
-      for (int t = 0; t < C::KS; ++t) {
-        qa[t] = lds_read16(qsb + 32 * qb * D + nrm[t]);
-        ga[t] = lds_read16(gsb + 32 * qb * D + nrm[t]);
-      }
-    };
-    auto sdp = [&](const u32x4_t* qa, const u32x4_t* ga, f32x16_t& s, f32x16_t& dp) {
+    // S = Q K^T and dP = dO V^T of block qb, with the row fragments read
+    // through a two-deep register ring (the reads of step t + 2 are issued as
+    // soon as the products of step t have taken their operands).
+    auto sdp = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, f32x16_t& s, f32x16_t& dp) {
+      const uint16_t* qrow = qsb + 32 * qb * D;
+      const uint16_t* grow = gsb + 32 * qb * D;
+      u32x4_t qa[2], ga[2];
+      qa[0] = lds_read16(qrow + nrm[0]);
+      ga[0] = lds_read16(grow + nrm[0]);
+      qa[1] = lds_read16(qrow + nrm[1]);
+      ga[1] = lds_read16(grow + nrm[1]);
       s = f32x16_t{};
       dp = f32x16_t{};
 #pragma unroll
       for (int t = 0; t < C::KS; ++t) {
-        s = mfma_bf16(qa[t], kf[t], s);
-        dp = mfma_bf16(ga[t], vf[t], dp);
+        s = mfma_bf16(qa[t & 1], kf[t], s);
+        dp = mfma_bf16(ga[t & 1], vf[t], dp);
+        if (t + 2 < C::KS) {
+          qa[t & 1] = lds_read16(qrow + nrm[t + 2]);
+          ga[t & 1] = lds_read16(grow + nrm[t + 2]);
+        }
       }
     };
     // P and dS of block qb as bf16 B operands (16 query rows each).
@@ -179,25 +188,27 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
                          pack_bf16(dsv[6], dsv[7])};
       }
     };
-    // dV^T += dO^T P and dK^T += Q^T dS for block qb (transpose reads, then products).
-    auto dvdk = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, const u32x4_t* pb, const u32x4_t* dsb) {
+    // dV^T += dO^T P and dK^T += Q^T dS for half u (16 query rows) of block qb:
+    // transpose reads of dO and Q, then the products.
+    struct TrFrags {
+      u32x2_t g[C::DB][2], x[C::DB][2];
+    };
+    auto read_tr = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, int u, TrFrags& f) {
+      const uint16_t* gblk = gsb + (32 * qb + 16 * u) * D;
+      const uint16_t* qblk = qsb + (32 * qb + 16 * u) * D;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint16_t* gblk = gsb + (32 * qb + 16 * u) * D;
-        const uint16_t* qblk = qsb + (32 * qb + 16 * u) * D;
-        u32x2_t gt[C::DB][2], xt[C::DB][2];
+      for (int db = 0; db < C::DB; ++db) {
+        f.g[db][0] = lds_read_tr(gblk + trd[db][0]);
+        f.g[db][1] = lds_read_tr(gblk + trd[db][1]);
+        f.x[db][0] = lds_read_tr(qblk + trd[db][0]);
+        f.x[db][1] = lds_read_tr(qblk + trd[db][1]);
+      }
+    };
+    auto dvdk_half = [&](const TrFrags& f, const u32x4_t& p, const u32x4_t& dsv) {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          gt[db][0] = lds_read_tr(gblk + trd[db][0]);
-          gt[db][1] = lds_read_tr(gblk + trd[db][1]);
-          xt[db][0] = lds_read_tr(qblk + trd[db][0]);
-          xt[db][1] = lds_read_tr(qblk + trd[db][1]);
-        }
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          dv[db] = mfma_bf16(u32x4_t{gt[db][0][0], gt[db][0][1], gt[db][1][0], gt[db][1][1]}, pb[u], dv[db]);
-          dk[db] = mfma_bf16(u32x4_t{xt[db][0][0], xt[db][0][1], xt[db][1][0], xt[db][1][1]}, dsb[u], dk[db]);
-        }
+      for (int db = 0; db < C::DB; ++db) {
+        dv[db] = mfma_bf16(u32x4_t{f.g[db][0][0], f.g[db][0][1], f.g[db][1][0], f.g[db][1][1]}, p, dv[db]);
+        dk[db] = mfma_bf16(u32x4_t{f.x[db][0][0], f.x[db][0][1], f.x[db][1][0], f.x[db][1][1]}, dsv, dk[db]);
       }
     };
 
@@ -207,29 +218,42 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
                     auto&& issue_next) {
       const int q0 = (qt_begin + idx % nq) * C::BM;
       issue_next();
-      // Blocks wholly before the wave's first key (causal) contribute nothing.
-      const bool skip0 = a.causal && q0 + 31 < wave_min_key;
       const bool mask_tile =
           (wave_max_key >= kvlim) || (a.causal && q0 < wave_max_key) || (q0 + C::BM > a.Tq);
+      // Pipeline over the two 32-row blocks:
+      //   S/dP(0);  [S/dP(1) | softmax(0)];  [dV/dK(0) | softmax(1)];  dV/dK(1)
+      // where [x | y] interleaves the products x with the vector work y.
       auto body = [&](auto mask_tag) {
-        u32x4_t qa[C::KS], ga[C::KS];
         f32x16_t s0, dp0, s1, dp1;
-        u32x4_t pb[2], dsb[2];
-        read_qg(qsb, gsb, 0, qa, ga);
-        sdp(qa, ga, s0, dp0);
-        read_qg(qsb, gsb, 1, qa, ga);
+        u32x4_t pb0[2], ds0[2], pb1[2], ds1[2];
+        TrFrags tf;
+        sdp(qsb, gsb, 0, s0, dp0);
         __builtin_amdgcn_sched_barrier(0);
-        sdp(qa, ga, s1, dp1);
-        softmax(mask_tag, ls, ds, q0, 0, s0, dp0, pb, dsb);
+        sdp(qsb, gsb, 1, s1, dp1);
+        softmax(mask_tag, ls, ds, q0, 0, s0, dp0, pb0, ds0);
 #pragma unroll
         for (int i = 0; i < 2 * C::KS; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
           __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then vector ALU work
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (!skip0) dvdk(qsb, gsb, 0, pb, dsb);
-        softmax(mask_tag, ls, ds, q0, 1, s1, dp1, pb, dsb);
-        dvdk(qsb, gsb, 1, pb, dsb);
+        read_tr(qsb, gsb, 0, 0, tf);
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk_half(tf, pb0[0], ds0[0]);
+        read_tr(qsb, gsb, 0, 1, tf);
+        softmax(mask_tag, ls, ds, q0, 1, s1, dp1, pb1, ds1);
+        for (int i = 0; i < 2 * C::DB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transpose reads
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then vector ALU work
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk_half(tf, pb0[1], ds0[1]);
+        read_tr(qsb, gsb, 1, 0, tf);
+        dvdk_half(tf, pb1[0], ds1[0]);
+        read_tr(qsb, gsb, 1, 1, tf);
+        dvdk_half(tf, pb1[1], ds1[1]);
       };
       if (mask_tile)
         body(std::true_type{});
