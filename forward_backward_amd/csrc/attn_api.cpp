@@ -8,7 +8,6 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
-#include <initializer_list>
 
 #include "attn_internal.h"
 
@@ -31,6 +30,21 @@ attn_status_t ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Element counts of the tensor families; a tensor with no elements may be NULL.
+struct Sizes {
+  long q, kv, stat;  // Q/O/dO/dQ, K/V/dK/dV, LSE
+};
+Sizes sizes_of(const attn_params_t* p) {
+  return Sizes{(long)p->B * p->Tq * p->Hq * p->D, (long)p->B * p->Tkv * p->Hkv * p->D, (long)p->B * p->Hq * p->Tq};
+}
+// A tensor pointer is acceptable when the tensor is empty, or non-NULL and 16-byte aligned.
+attn_status_t check_ptr(const void* ptr, long count, bool need_align) {
+  if (count == 0) return ATTN_OK;
+  if (ptr == nullptr) return ATTN_ERR_INVALID;
+  if (need_align && !aligned16(ptr)) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
 
 constexpr long kMaxGrid = 2147483647L;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -78,9 +92,10 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
                        void* stream) {
   attn_status_t st = attn_validate(p, ATTN_OP_FWD);
   if (st != ATTN_OK) return st;
-  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_INVALID, "null tensor pointer");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const Sizes n = sizes_of(p);
+  if (check_ptr(q, n.q, true) || check_ptr(k, n.kv, true) || check_ptr(v, n.kv, true) || check_ptr(o, n.q, true) ||
+      check_ptr(lse, n.stat, false))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   attn::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
@@ -122,18 +137,6 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
   return ATTN_OK;
 }
 
-bool all_aligned(std::initializer_list<const void*> ps) {
-  for (const void* x : ps)
-    if (!aligned16(x)) return false;
-  return true;
-}
-
-bool none_null(std::initializer_list<const void*> ps) {
-  for (const void* x : ps)
-    if (x == nullptr) return false;
-  return true;
-}
-
 attn_status_t run_pass(const attn_params_t* p, const attn::BwdArgs& a, int pass, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = p->dtype == ATTN_BF16 ? attn::launch_bwd_pass_bf16(a, p->D, pass, s)
@@ -151,8 +154,9 @@ attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const f
   attn::BwdArgs a;
   attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  if (!none_null({o, lse, dout})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
-  if (!all_aligned({o, dout})) return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const Sizes n = sizes_of(p);
+  if (check_ptr(o, n.q, true) || check_ptr(lse, n.stat, false) || check_ptr(dout, n.q, true))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   a.o = o; a.lse = lse; a.dout = dout;
   return run_pass(p, a, attn::kBwdPre, stream);
 }
@@ -163,8 +167,11 @@ attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k
   attn::BwdArgs a;
   attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  if (!none_null({q, k, v, lse, dout, dk, dv})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
-  if (!all_aligned({q, k, v, dout, dk, dv})) return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const Sizes n = sizes_of(p);
+  if (check_ptr(q, n.q, true) || check_ptr(k, n.kv, true) || check_ptr(v, n.kv, true) ||
+      check_ptr(lse, n.stat, false) || check_ptr(dout, n.q, true) || check_ptr(dk, n.kv, true) ||
+      check_ptr(dv, n.kv, true))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   a.q = q; a.k = k; a.v = v; a.lse = lse; a.dout = dout; a.dk = dk; a.dv = dv;
   return run_pass(p, a, attn::kBwdDkdv, stream);
 }
@@ -174,8 +181,10 @@ attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, 
   attn::BwdArgs a;
   attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  if (!none_null({q, k, v, lse, dout, dq})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
-  if (!all_aligned({q, k, v, dout, dq})) return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const Sizes n = sizes_of(p);
+  if (check_ptr(q, n.q, true) || check_ptr(k, n.kv, true) || check_ptr(v, n.kv, true) ||
+      check_ptr(lse, n.stat, false) || check_ptr(dout, n.q, true) || check_ptr(dq, n.q, true))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   a.q = q; a.k = k; a.v = v; a.lse = lse; a.dout = dout; a.dq = dq;
   return run_pass(p, a, attn::kBwdDq, stream);
 }
@@ -186,9 +195,11 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
   attn::BwdArgs a;
   attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
   if (st != ATTN_OK) return st;
-  if (!none_null({q, k, v, o, lse, dout, dq, dk, dv})) return fail(ATTN_ERR_INVALID, "null tensor pointer");
-  if (!all_aligned({q, k, v, o, dout, dq, dk, dv}))
-    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const Sizes n = sizes_of(p);
+  if (check_ptr(q, n.q, true) || check_ptr(k, n.kv, true) || check_ptr(v, n.kv, true) || check_ptr(o, n.q, true) ||
+      check_ptr(lse, n.stat, false) || check_ptr(dout, n.q, true) || check_ptr(dq, n.q, true) ||
+      check_ptr(dk, n.kv, true) || check_ptr(dv, n.kv, true))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
   for (int pass : {attn::kBwdPre, attn::kBwdDkdv, attn::kBwdDq}) {
     st = run_pass(p, a, pass, stream);
@@ -228,9 +239,10 @@ attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_c
                           float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   attn_status_t st = attn_validate(p, ATTN_OP_DECODE);
   if (st != ATTN_OK) return st;
-  if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID, "null tensor pointer");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return fail(ATTN_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const Sizes n = sizes_of(p);
+  if (check_ptr(q, n.q, true) || check_ptr(k_cache, n.kv, true) || check_ptr(v_cache, n.kv, true) ||
+      check_ptr(o, n.q, true))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   if (num_splits < 0) return fail(ATTN_ERR_INVALID, "num_splits must be >= 0 (0 = automatic)");
   if (num_splits == 0) num_splits = attn_decode_num_splits(p);
   const size_t need = attn_decode_workspace_size(p, num_splits);
