@@ -208,31 +208,33 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
   return ok();
 }
 
-int32_t attn_decode_num_splits(const attn_params_t* p) {
-  if (p == nullptr || p->Tkv <= 0) return 1;
-  // Fixed key range per split (a pure function of the shape): 512 keys, so
-  // that a batch's active splits scale with its KV length and every split
-  // streams the same amount of K/V.
-  const int split_len = 512;
-  int s = (p->Tkv + split_len - 1) / split_len;
-  return s < 1 ? 1 : s;
+// Packed query rows (Tq * G) of one (batch, KV head) in blocks of the decode tile.
+static long decode_row_blocks(const attn_params_t* p) {
+  const long rows = (long)(p->Tq > 0 ? p->Tq : 0) * (p->Hkv > 0 && p->Hq >= p->Hkv ? p->Hq / p->Hkv : 0);
+  return (rows + attn::kDecodeRows - 1) / attn::kDecodeRows;
 }
 
-static int decode_split_len(const attn_params_t* p, int num_splits) {
-  const int t = attn::kDecodeTileN;
-  int per = (p->Tkv + num_splits - 1) / num_splits;
-  per = (per + t - 1) / t * t;
-  return per < t ? t : per;
+static long decode_segments(const attn_params_t* p) {
+  return (long)(p->B > 0 ? p->B : 0) * (p->Hkv > 0 ? p->Hkv : 0) * decode_row_blocks(p);
+}
+
+int32_t attn_decode_num_splits(const attn_params_t* p) {
+  if (p == nullptr) return 1;
+  // One workgroup per compute unit at D = 128 (its LDS ring takes 128 KiB),
+  // two at D = 64; the budget leaves room for the up to one extra range per
+  // segment that rounding adds, so that all ranges run in one wave.
+  const long resident = (long)attn::kDecodeSlots * (p->D == 64 ? 2 : 1);
+  const long budget = resident - decode_segments(p);
+  return budget < 1 ? 1 : (int32_t)budget;
 }
 
 size_t attn_decode_workspace_size(const attn_params_t* p, int32_t num_splits) {
-  if (p == nullptr || p->Hkv < 1 || p->Hq < p->Hkv) return 0;
+  if (p == nullptr || p->Hkv < 1 || p->Hq < p->Hkv || p->D < 1) return 0;
   if (num_splits <= 0) num_splits = attn_decode_num_splits(p);
-  const size_t rows = (size_t)(p->B > 0 ? p->B : 0) * p->Hkv * num_splits * (size_t)(p->Tq > 0 ? p->Tq : 0) *
-                      (p->Hq / p->Hkv);
-  const size_t o_bytes = round_up(rows * (size_t)p->D * sizeof(float), 256);
-  const size_t l_bytes = round_up(rows * sizeof(float), 256);
-  return o_bytes + l_bytes;
+  const long segs = decode_segments(p);
+  if (segs == 0) return 0;
+  const size_t rows = (size_t)(num_splits + segs) * attn::kDecodeRows;
+  return round_up(rows * (size_t)p->D * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
 attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache, void* o,
@@ -248,19 +250,19 @@ attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_c
   const size_t need = attn_decode_workspace_size(p, num_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "workspace too small (%d bytes needed)", (int)need);
-  const long rows = (long)p->B * p->Hkv * num_splits;
-  if (rows >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "too many splits");
+  const long segs = decode_segments(p);
+  if ((long)num_splits + segs >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "too many splits");
   attn::DecodeArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_lens = p->kv_lens;
-  const size_t prow = (size_t)p->B * p->Hkv * num_splits * (size_t)p->Tq * (p->Hq / p->Hkv);
+  const size_t rows = (size_t)(num_splits + segs) * attn::kDecodeRows;
   a.part_o = static_cast<float*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(prow * p->D * sizeof(float), 256));
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * p->D * sizeof(float), 256));
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e;
-  a.num_splits = num_splits;
-  a.split_len = decode_split_len(p, num_splits);
+  a.budget = num_splits;
+  a.num_rblocks = (int)decode_row_blocks(p);
+  a.num_slots = (int)(num_splits + segs);
   hipError_t e = attn::launch_decode_bf16(a, p->D, static_cast<hipStream_t>(stream));
-  if (e == hipErrorNotSupported) return fail(ATTN_ERR_UNSUPPORTED, "no kernel for this configuration");
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
   return ok();
 }

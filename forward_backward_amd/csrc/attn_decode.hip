@@ -6,48 +6,138 @@
 // across workgroups, packs the query heads of a GQA group into one tile and
 // combines the partial results with their log-sum-exp.
 //
-// Split kernel: one workgroup per (batch, KV head, split, 64 packed rows).
-// Packed row p = i * G + g is query i of query head KV_head * G + g. Split s
-// covers keys [s * L, min((s + 1) * L, kv_len[b])); splits past the length
-// exit at once. Four waves: wave w handles packed rows 32 * (w % 2) .. + 31
-// and key block w / 2 of every 64-key tile; the two waves of a row block
-// merge their (max, sum, O) through LDS at the end. The partial output is
-// written normalised, in fp32, with its natural-log LSE.
+// Packed row p = i * G + g is query i of query head KV_head * G + g. A
+// segment is one (batch, KV head, block of 64 packed rows); its n_b =
+// ceil(kv_len[b] / 64) key tiles are cut into k_b = min(n_b, ceil(n_b * P / U))
+// near-equal ranges, U being the key tiles of all segments and P the split
+// budget. Every range therefore holds at most ceil(U / P) tiles whatever the
+// KV lengths are, and there are at most P + (number of segments) ranges; the
+// schedule is computed on the device from kv_lens by both kernels. Range
+// number r (counting segments in order, then ranges within a segment) is
+// workgroup r of the split kernel and partial slot r of the workspace.
 //
-// Combine kernel: for each output row, the splits are merged in ascending
-// order: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s. A row
-// with no valid key gets O = 0 and LSE = -inf.
+// Split kernel: four waves; wave w handles packed rows 32 * (w % 2) .. + 31
+// and key block w / 2 of every 64-key tile. K/V tiles stream through a
+// four-stage LDS ring filled by direct global->LDS copies (three tiles in
+// flight while one is computed); keys at or past the length are never read.
+// The two waves of a row block merge their (max, sum, O) through LDS at the
+// end and write the normalised fp32 partial output with its natural-log LSE.
+//
+// Combine kernel: for each output row the ranges of its segment are merged
+// in ascending order with a running maximum: LSE = log sum_r exp(LSE_r),
+// O = sum_r exp(LSE_r - LSE) O_r. A row with no valid key gets O = 0 and
+// LSE = -inf.
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
 namespace attn {
 namespace {
 
-constexpr float kLn2 = 0.6931471805599453f;
-
 template <int D>
 struct DecCfg {
-  static constexpr int ROWS = 64;             // packed rows per workgroup
+  static constexpr int ROWS = kDecodeRows;    // packed rows per workgroup
   static constexpr int BN = kDecodeTileN;     // 64 keys per tile
   static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KSTRIDE = D + 8;
-  static constexpr int VSTRIDE = D + 16;
-  static constexpr int KTILE = BN * KSTRIDE;
-  static constexpr int VTILE = BN * VSTRIDE;
-  static constexpr int CPR = D / 8;
-  static constexpr int CPT = BN * CPR / THREADS;
-  static_assert(BN * CPR % THREADS == 0, "tile must split evenly");
+  static constexpr int TILE = BN * D;         // elements of one K or V tile (swizzled, unpadded)
+  static constexpr int NST = 4;               // LDS ring stages
+  // Global->LDS copy instructions per wave per stage (K and V): 1 KiB each.
+  static constexpr int COPIES = 2 * TILE * 2 / 1024 / (THREADS / 64);
   // LDS for the final merge: per row block, O (16 * DB floats per lane) plus max and sum.
   static constexpr int MERGE_FLOATS = 2 * 64 * (16 * DB + 2);
-  static_assert(MERGE_FLOATS * 4 <= 2 * (KTILE + VTILE) * 2, "merge area must fit in the staging buffers");
+  static_assert(MERGE_FLOATS * 4 <= NST * 2 * TILE * 2, "merge area must fit in the ring");
+  static_assert(ROWS == 64, "two row blocks of 32");
 };
+
+// s_waitcnt vmcnt(N) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most min(later, MAXL) tiles of COPIES copies each are in flight.
+template <int MAXL, int COPIES>
+__device__ __forceinline__ void wait_tile(int later) {
+  if constexpr (MAXL > 0) {
+    if (later >= MAXL) {
+      wait_vmem_le<MAXL * COPIES>();
+      return;
+    }
+    wait_tile<MAXL - 1, COPIES>(later);
+  } else {
+    wait_vmem_le<0>();
+  }
+}
+
+__device__ __forceinline__ int key_tiles(const DecodeArgs& a, int b) {
+  return (clamp_len(a.kv_lens, b, a.Tkv) + kDecodeTileN - 1) / kDecodeTileN;
+}
+
+// Ranges of a segment with n tiles out of U in total: min(n, ceil(n * P / U)).
+__device__ __forceinline__ int num_ranges(int n, int P, long U) {
+  if (n == 0) return 0;
+  const unsigned long num = (unsigned long)n * (unsigned)P + (unsigned long)(U - 1);
+  unsigned long k;
+  if ((num >> 32) == 0 && (U >> 32) == 0)
+    k = (unsigned)num / (unsigned)U;  // 32-bit division when the operands fit
+  else
+    k = num / (unsigned long)U;
+  return k < (unsigned long)n ? (int)k : n;
+}
+
+__device__ __forceinline__ long wave_sum(long x) {
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ long wave_incl_scan(long x, int lane) {
+  for (int off = 1; off < 64; off <<= 1) {
+    const long y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// The schedule is evaluated by every wave on its own, lane i taking batch
+// b0 + i of each chunk of 64 batches, so its cost grows with B / 64.
+
+// U: key tiles of all segments.
+__device__ __forceinline__ long total_tiles(const DecodeArgs& a, int lane) {
+  long s = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    s += wave_sum(bb < a.B ? key_tiles(a, bb) : 0);
+  }
+  return s * a.Hkv * a.num_rblocks;
+}
+
+// Batch b's first slot (ranges of earlier batches) and its ranges per segment.
+__device__ __forceinline__ void batch_slots(const DecodeArgs& a, long U, int b, int lane, long& first, int& k) {
+  long cum = 0;
+  first = 0;
+  k = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int kb = bb < a.B ? num_ranges(key_tiles(a, bb), a.budget, U) : 0;
+    const long cnt = (long)a.Hkv * a.num_rblocks * kb;
+    const long incl = wave_incl_scan(cnt, lane) + cum;
+    const int src = b - b0 < 0 ? 0 : (b - b0 > 63 ? 63 : b - b0);
+    const long excl_src = __shfl(incl - cnt, src, 64);
+    const int k_src = __shfl(kb, src, 64);
+    if (b >= b0 && b < b0 + 64) {
+      first = excl_src;
+      k = k_src;
+    }
+    cum = __shfl(incl, 63, 64);
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   using C = DecCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::KTILE + C::VTILE)];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[C::NST * 2 * C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -57,26 +147,61 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   const int rb = wave & 1;   // row block
   const int kk = wave >> 1;  // key block within each tile
 
+  // Find this workgroup's range (the same in every wave).
+  const long U = total_tiles(a, lane);
+  if (U == 0) return;
+  const int slot = blockIdx.x;
+  int b = -1, n = 0, k = 0, local = 0;
+  {
+    long cum = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int bb = b0 + lane;
+      const int nb = bb < a.B ? key_tiles(a, bb) : 0;
+      const int kb = num_ranges(nb, a.budget, U);
+      const long cnt = (long)a.Hkv * a.num_rblocks * kb;
+      const long incl = wave_incl_scan(cnt, lane) + cum;
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64((long)slot < incl);
+      if (hit != 0) {
+        const int L = __builtin_ctzll(hit);
+        b = b0 + L;
+        n = __shfl(nb, L, 64);
+        k = __shfl(kb, L, 64);
+        local = (int)(slot - (__shfl(incl, L, 64) - __shfl(cnt, L, 64)));
+        break;
+      }
+      cum = __shfl(incl, 63, 64);
+    }
+  }
+  if (b < 0) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  n = __builtin_amdgcn_readfirstlane(n);
+  k = __builtin_amdgcn_readfirstlane(k);
+  local = __builtin_amdgcn_readfirstlane(local);
+  const int seg = local / k;       // (KV head, row block) within the batch
+  const int j = local % k;         // range within the segment
+  const int kh = seg / a.num_rblocks;
+  const int rbi = seg % a.num_rblocks;
+  const int t_begin = (int)((long)j * n / k);
+  const int t_end = (int)((long)(j + 1) * n / k);
+  const int ntiles = t_end - t_begin;  // >= 1 since k <= n
+  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
+
   const int G = a.Hq / a.Hkv;
   const int R = a.Tq * G;
-  const int nrb = (R + C::ROWS - 1) / C::ROWS;
-  int id = blockIdx.x;
-  const int rbi = id % nrb;
-  id /= nrb;
-  const int s = id % a.num_splits;
-  id /= a.num_splits;
-  const int kh = id % a.Hkv;
-  const int b = id / a.Hkv;
-
-  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
-  const int kbeg = s * a.split_len;
-  if (kbeg >= kvlim) return;  // the combine ignores splits past the length
-  const int kend = min(kbeg + a.split_len, kvlim);
-  const int ntiles = (kend - kbeg + C::BN - 1) / C::BN;
-
   const long krs = (long)a.Hkv * D;
   const uint16_t* kb = (const uint16_t*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const uint16_t* vb = (const uint16_t*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
+
+  auto issue = [&](int t) {
+    uint16_t* st = ring + ((t - t_begin) % C::NST) * 2 * C::TILE;
+    dma_tile<D, C::BN, C::THREADS>(st, kb, krs, t * C::BN, kvlim, tid);
+    dma_tile<D, C::BN, C::THREADS>(st + C::TILE, vb, krs, t * C::BN, kvlim, tid);
+  };
+  // Fill the ring before anything else so that the first tiles are on their
+  // way while Q is loaded.
+#pragma unroll
+  for (int i = 0; i < C::NST - 1; ++i)
+    if (i < ntiles) issue(t_begin + i);
 
   const int prow = rbi * C::ROWS + 32 * rb + l32;  // packed row of this lane
   const bool row_ok = prow < R;
@@ -87,6 +212,11 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
     const uint16_t* qp = (const uint16_t*)a.q + (((long)b * a.Tq + i) * a.Hq + kh * G + g) * D;
 #pragma unroll
     for (int t = 0; t < C::KS; ++t) qf[t] = row_ok ? gload16(qp + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    // Take Q here: the compiler cannot see the ring copies, and a first use
+    // of Q inside the loop would make it wait for all loads (the copies
+    // included) on every iteration.
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) asm volatile("" ::"v"(qf[t]));
   }
 
   f32x16_t o[C::DB];
@@ -95,57 +225,39 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   float m = -INFINITY, lsum = 0.f;
   const float c = a.scale_log2;
 
-  u32x4_t kr[C::CPT], vr[C::CPT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + C::THREADS * i;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      const int key = k0 + row;
-      if (key < kend) {
-        kr[i] = gload16(kb + key * krs + cc * 8);
-        vr[i] = gload16(vb + key * krs + cc * 8);
-      } else {
-        kr[i] = u32x4_t{0, 0, 0, 0};
-        vr[i] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* kl = lds + buf * (C::KTILE + C::VTILE);
-    uint16_t* vl = kl + C::KTILE;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + C::THREADS * i;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      lds_write16(kl + row * C::KSTRIDE + cc * 8, kr[i]);
-      lds_write16(vl + row * C::VSTRIDE + cc * 8, vr[i]);
-    }
-  };
-
-  gload(kbeg);
-  lstore(0);
-  __syncthreads();
-
+  // Swizzled LDS offsets of this lane's reads; the key block (32 rows) and
+  // the 16-row steps keep the swizzle, which depends on the row's low 4 bits.
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int nrm[C::KS], trd[C::DB][2];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh) + 32 * kk * D;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    trd[db][0] = swz_off<D>(tr_row, 32 * db + tr_col) + 32 * kk * D;
+    trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col) + 32 * kk * D;
+  }
 
   for (int it = 0; it < ntiles; ++it) {
-    const int k0 = kbeg + it * C::BN;
-    if (it + 1 < ntiles) gload(k0 + C::BN);
-    const uint16_t* kl = lds + (it & 1) * (C::KTILE + C::VTILE) + (32 * kk) * C::KSTRIDE;
-    const uint16_t* vl = lds + (it & 1) * (C::KTILE + C::VTILE) + C::KTILE + (32 * kk) * C::VSTRIDE;
+    // Tile `it` has landed once at most the copies of the (up to NST - 2)
+    // later tiles already issued are outstanding; the barrier makes every wave's
+    // share visible and retires the stage the next copy overwrites.
+    wait_tile<C::NST - 2, C::COPIES>(ntiles - 1 - it);
+    __syncthreads();
+    if (it + C::NST - 1 < ntiles) issue(t_begin + it + C::NST - 1);
 
+    const uint16_t* kl = ring + (it % C::NST) * 2 * C::TILE;
+    const uint16_t* vl = kl + C::TILE;
     f32x16_t sc = f32x16_t{};
 #pragma unroll
-    for (int t = 0; t < C::KS; ++t) sc = mfma_bf16(lds_read16(kl + l32 * C::KSTRIDE + 16 * t + 8 * hh), qf[t], sc);
+    for (int t = 0; t < C::KS; ++t) sc = mfma_bf16(lds_read16(kl + nrm[t]), qf[t], sc);
 
-    const int kblk = k0 + 32 * kk;
-    if (kblk + 32 > kend) {
+    const int kblk = (t_begin + it) * C::BN + 32 * kk;
+    if (kblk + 32 > kvlim) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kblk + 8 * (r >> 2) + 4 * hh + (r & 3);
-        sc[r] = key < kend ? sc[r] : -INFINITY;
+        sc[r] = key < kvlim ? sc[r] : -INFINITY;
       }
     }
     float mt = -INFINITY;
@@ -172,21 +284,19 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
       const int r0 = 8 * u;
       const u32x4_t pf = u32x4_t{pack_bf16(sc[r0 + 0], sc[r0 + 1]), pack_bf16(sc[r0 + 2], sc[r0 + 3]),
                                  pack_bf16(sc[r0 + 4], sc[r0 + 5]), pack_bf16(sc[r0 + 6], sc[r0 + 7])};
-      const uint16_t* vrow = vl + (16 * u + tr_row) * C::VSTRIDE + tr_col;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const u32x2_t lo = lds_read_tr(vrow + 32 * db);
-        const u32x2_t hi = lds_read_tr(vrow + 8 * C::VSTRIDE + 32 * db);
+        const u32x2_t lo = lds_read_tr(vl + trd[db][0] + 16 * u * D);
+        const u32x2_t hi = lds_read_tr(vl + trd[db][1] + 16 * u * D);
         o[db] = mfma_bf16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf, o[db]);
       }
     }
-
-    if (it + 1 < ntiles) lstore((it + 1) & 1);
-    __syncthreads();
   }
 
-  // Merge the two key blocks of each row block (waves rb and rb + 2).
-  float* mg = reinterpret_cast<float*>(lds) + rb * 64 * (16 * C::DB + 2);
+  // Merge the two key blocks of each row block (waves rb and rb + 2). Every
+  // copy has completed (the last iteration waited for all of them).
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(ring) + rb * 64 * (16 * C::DB + 2);
   if (kk == 1) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -206,7 +316,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
     const float ltot = half_sum(lsum * a0 + l1 * a1);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (row_ok) {
-      const long prt = (((long)b * a.Hkv + kh) * a.num_splits + s) * R + prow;
+      const long prt = (long)slot * C::ROWS + 32 * rb + l32;
       float* po = a.part_o + prt * D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -226,36 +336,66 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
 }
 
 // One group of D/4 threads per output row (packed order), 4 head_dim
-// elements per thread, splits merged in ascending order.
+// elements per thread; the segment's ranges are merged in ascending order.
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(DecodeArgs a) {
   constexpr int TPR = D / 4;
   const int G = a.Hq / a.Hkv;
   const int R = a.Tq * G;
   const long gt = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gt / TPR;  // ((b * Hkv + kh) * R + p)
+  const long nrows = (long)a.B * a.Hkv * R;
+  // Threads past the last row stay until the schedule (a whole-wave
+  // computation) is done.
+  const bool row_ok = gt / TPR < nrows;
+  const long row = row_ok ? gt / TPR : nrows - 1;  // ((b * Hkv + kh) * R + p)
   const int part = (int)(gt % TPR);
-  if (row >= (long)a.B * a.Hkv * R) return;
   const int p = (int)(row % R);
   const int kh = (int)((row / R) % a.Hkv);
   const int b = (int)(row / ((long)R * a.Hkv));
-  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
-  const int nact = (kvlim + a.split_len - 1) / a.split_len;
-  const long base = ((long)b * a.Hkv + kh) * a.num_splits * R + p;
+  const int rbi = p / kDecodeRows;
 
-  float lmax = -INFINITY;
-  for (int s = 0; s < nact; ++s) lmax = fmaxf(lmax, a.part_lse[base + (long)s * R]);
+  // First slot and number of ranges of this row's segment (same schedule as
+  // the split kernel).
+  const long U = total_tiles(a, threadIdx.x & 63);
+  long first = 0;
+  int k = 0;
+  if (U > 0) {
+    batch_slots(a, U, b, threadIdx.x & 63, first, k);
+    first += (long)(kh * a.num_rblocks + rbi) * k;
+  }
+  if (!row_ok) return;
+
+  // Ranges in chunks of 8 whose loads are all issued before any is used
+  // (one memory round trip per chunk); running maximum across chunks.
+  constexpr int CH = 8;
+  const int prow = p % kDecodeRows;
+  float lmax = -INFINITY, tot = 0.f;
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  if (lmax != -INFINITY) {
-    for (int s = 0; s < nact; ++s) {
-      const long pr = base + (long)s * R;
-      const float ls = a.part_lse[pr];
-      const float w = ls == -INFINITY ? 0.f : __expf(ls - lmax);
-      const f32x4_t v = *(const f32x4_t*)(a.part_o + pr * D + 4 * part);
-      acc += w * v;
+  for (int r0 = 0; r0 < k; r0 += CH) {
+    float ls[CH];
+    f32x4_t v[CH];
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+      const bool ok = r0 + x < k;
+      const long pr = (first + (ok ? r0 + x : r0)) * kDecodeRows + prow;
+      ls[x] = ok ? a.part_lse[pr] : -INFINITY;
+      v[x] = ok ? *(const f32x4_t*)(a.part_o + pr * D + 4 * part) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float cm = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < CH; ++x) cm = fmaxf(cm, ls[x]);
+    const float mnew = fmaxf(lmax, cm);
+    if (mnew == -INFINITY) continue;
+    const float s_old = lmax == -INFINITY ? 0.f : __expf(lmax - mnew);
+    acc *= s_old;
+    tot *= s_old;
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+      const float w = ls[x] == -INFINITY ? 0.f : __expf(ls[x] - mnew);
+      acc += w * v[x];
       tot += w;
     }
+    lmax = mnew;
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   const int i = p / G, g = p % G;
@@ -271,9 +411,8 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const long R = (long)a.Tq * G;
   if (R == 0 || a.B == 0) return;
-  const long nrb = (R + DecCfg<D>::ROWS - 1) / DecCfg<D>::ROWS;
-  const long blocks = (long)a.B * a.Hkv * a.num_splits * nrb;
-  hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (a.Tkv > 0)
+    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3((unsigned)a.num_slots), dim3(256), 0, st, a);
   const long threads = (long)a.B * a.Hkv * R * (D / 4);
   hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
 }

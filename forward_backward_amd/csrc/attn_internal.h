@@ -51,14 +51,15 @@ struct DecodeArgs {
   const void* v;
   void* o;
   float* lse;              // optional [B, Hq, Tq]
-  float* part_o;           // workspace [B, Hkv, S, Tq*G, D] fp32
-  float* part_lse;         // workspace [B, Hkv, S, Tq*G] fp32 (natural log)
+  float* part_o;           // workspace [slots, kDecodeRows, D] fp32
+  float* part_lse;         // workspace [slots, kDecodeRows] fp32 (natural log)
   const int32_t* kv_lens;
   int B, Tq, Tkv, Hq, Hkv;
   float scale;
   float scale_log2;
-  int num_splits;          // S
-  int split_len;           // keys per split (a multiple of the key tile)
+  int budget;              // P: key ranges are sized as if P workgroups shared all key tiles
+  int num_rblocks;         // packed row blocks per (batch, KV head)
+  int num_slots;           // P + B * Hkv * num_rblocks (upper bound on the key ranges)
 };
 
 // Launchers (each returns the hipGetLastError() after its launches).
@@ -75,5 +76,7 @@ constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
 constexpr int kBwdBlockM = 64;    // query rows per dQ workgroup
 constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
 constexpr int kDecodeTileN = 64;  // keys per decode iteration
+constexpr int kDecodeRows = 64;   // packed query rows per decode workgroup
+constexpr int kDecodeSlots = 256; // decode workgroups resident at once (one per compute unit)
 
 }  // namespace attn

@@ -15,6 +15,10 @@ SMALL = [
     Case("dec_q32_g4_rows128", 1, 32, 1500, 8, 2, 128, kv_lens=(1500,), workload_id=202, decode=True),
     Case("dec_d64_q5_g8", 2, 5, 2048, 16, 2, 64, kv_lens=(0, 2048), workload_id=203, decode=True),
     Case("dec_nomask_q3", 1, 3, 1100, 4, 4, 64, workload_id=204, decode=True),
+    # more than 64 batches: the on-device range schedule works in chunks of 64
+    Case("dec_b70_kvrange", 70, 1, 300, 2, 1, 64, kv_len_range=(0, 300), workload_id=205, decode=True),
+    # packed rows over two row blocks (Tq * G = 80)
+    Case("dec_q20_g4_two_rowblocks", 2, 20, 900, 8, 2, 128, kv_lens=(900, 77), workload_id=206, decode=True),
 ]
 
 
@@ -47,7 +51,7 @@ def test_decode_small(case):
     check_decode(case)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 64])
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 1000])
 def test_decode_split_count_changes_rounding_only(splits):
     check_decode(SMALL[1], num_splits=splits)
 
