@@ -21,7 +21,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
  *     in [B, T, H, D] order (row stride H*D elements) and 16-byte aligned.
  *     Q, dO, O, dQ: [B, Tq, Hq, D]; K, V, dK, dV: [B, Tkv, Hkv, D].
- *     Tensors are bf16 or fp32 as given by attn_params_t.dtype.
+ *     Tensors are bf16 or fp32 as given by attn_params_t.dtype. A tensor
+ *     with no elements (B, Tq or Tkv = 0) may be passed as NULL; any other
+ *     NULL or misaligned tensor pointer -> ATTN_ERR_INVALID.
  *   - LSE is fp32 [B, Hq, Tq], natural logarithm, -inf on rows with no
  *     valid key (where O is 0).
  *   - kv_lens, when not NULL, is a DEVICE int32 [B]; each value is clamped
@@ -108,22 +110,34 @@ attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k
 attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
                           const void* dout, void* dq, const void* workspace, size_t workspace_bytes, void* stream);
 
-/* Split count attn_decode uses when num_splits = 0 (a pure function of the
- * shape, so reruns are bitwise identical). */
+/* Split budget attn_decode uses when num_splits = 0: sized so that every key
+ * range of the call runs at once on the chip (a pure function of the shape,
+ * so reruns are bitwise identical). */
 int32_t attn_decode_num_splits(const attn_params_t* p);
 
-/* Bytes of device workspace attn_decode needs for `num_splits` (0 = auto):
- * fp32 partial outputs and partial LSEs per split. */
+/* Bytes of device workspace attn_decode needs for the split budget
+ * `num_splits` (0 = auto): fp32 partial outputs and partial LSEs for at most
+ * num_splits + B * Hkv * ceil(Tq * Hq / Hkv / 64) key ranges of 64 packed
+ * rows each. */
 size_t attn_decode_workspace_size(const attn_params_t* p, int32_t num_splits);
 
 /* Split-KV decode ("Attention performance", section "Grouped-query attention
- * and decoding"): few queries over a long KV cache. The keys are split
- * across workgroups, the Tq queries of the G heads of a KV group are packed
- * into one tile, and the partial results are combined by their LSE in a
- * fixed split order. Non-causal (p->causal must be 0); bf16 only.
- * q [B,Tq,Hq,D]; k_cache/v_cache [B,Tkv,Hkv,D] (Tkv = capacity);
- * kv_lens = valid length per batch (NULL = Tkv). o [B,Tq,Hq,D] bf16;
- * lse fp32 [B,Hq,Tq] or NULL. */
+ * and decoding"): few queries over a long KV cache. The Tq queries of the G
+ * query heads of a KV head are packed into tiles of 64 rows (row i * G + g),
+ * the keys are split across workgroups, and the partial results are
+ * combined by their LSE in a fixed order. The split is balanced over the
+ * actual lengths: with U the 64-key tiles of all (batch, KV head, row tile)
+ * segments and P = num_splits (the split budget; 0 = automatic), a segment
+ * with n tiles is cut into min(n, ceil(n * P / U)) near-equal key ranges, so
+ * no range exceeds ceil(U / P) tiles. The schedule is computed on the device
+ * from kv_lens; results depend on it only through rounding and are bitwise
+ * reproducible for the same inputs and budget.
+ * Non-causal (p->causal must be 0); bf16 only.
+ * q [B,Tq,Hq,D]; k_cache/v_cache [B,Tkv,Hkv,D] (Tkv = capacity); keys at or
+ * past kv_lens[b] are never read. kv_lens = valid length per batch (NULL =
+ * Tkv). o [B,Tq,Hq,D] bf16; lse fp32 [B,Hq,Tq] or NULL. A row with no valid
+ * key gets O = 0 and LSE = -inf. num_splits < 0 -> ATTN_ERR_INVALID; a
+ * workspace smaller than attn_decode_workspace_size -> ATTN_ERR_WORKSPACE. */
 attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache,
                           void* o, float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);
