@@ -71,6 +71,9 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   if (op == ATTN_OP_DECODE && p->causal) return fail(ATTN_ERR_INVALID, "decode is non-causal");
   if (p->D != 64 && p->D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", p->D);
   if (op == ATTN_OP_DECODE && p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is bf16 only");
+  // Tile copies address a tile's rows with 32-bit byte offsets.
+  if ((long)p->Hq * p->D > (1L << 22) || (long)p->Hkv * p->D > (1L << 22))
+    return fail(ATTN_ERR_UNSUPPORTED, "heads * head_dim above 2^22 (Hq = %d, Hkv = %d)", p->Hq, p->Hkv);
   const long qrows = (long)p->B * p->Hq * p->Tq;
   const long krows = (long)p->B * p->Hkv * p->Tkv;
   if (qrows >= kMaxGrid || krows >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");

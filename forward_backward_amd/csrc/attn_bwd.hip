@@ -122,12 +122,18 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
       trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col);
     }
 
+    const TileCopy<D, C::BM, C::THREADS> qcopy(qrs, tid);
     auto issue = [&](int idx, uint16_t* qs, uint16_t* gs, float* ls, float* ds) {
       const int h = kh * G + idx / nq;
       const int q0 = (qt_begin + idx % nq) * C::BM;
       const long hoff = ((long)b * a.Tq * a.Hq + h) * D;
-      dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
-      dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
+      if (q0 + C::BM <= a.Tq) {
+        qcopy.copy(qs, (const uint16_t*)a.q + hoff, qrs, q0);
+        qcopy.copy(gs, (const uint16_t*)a.dout + hoff, qrs, q0);
+      } else {
+        dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
+        dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
+      }
       const long stat0 = ((long)b * a.Hq + h) * a.Tq;
       static_assert(C::BM == 64, "row statistics are copied by two waves of 64 lanes");
       if (wave == 0) dma_row64(ls, a.lse2 + stat0, q0, a.Tq, lane);

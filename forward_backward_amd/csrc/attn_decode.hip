@@ -192,10 +192,16 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   const uint16_t* kb = (const uint16_t*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const uint16_t* vb = (const uint16_t*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
 
+  const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
   auto issue = [&](int t) {
     uint16_t* st = ring + ((t - t_begin) % C::NST) * 2 * C::TILE;
-    dma_tile<D, C::BN, C::THREADS>(st, kb, krs, t * C::BN, kvlim, tid);
-    dma_tile<D, C::BN, C::THREADS>(st + C::TILE, vb, krs, t * C::BN, kvlim, tid);
+    if ((t + 1) * C::BN <= kvlim) {
+      kvcopy.copy(st, kb, krs, t * C::BN);
+      kvcopy.copy(st + C::TILE, vb, krs, t * C::BN);
+    } else {
+      dma_tile<D, C::BN, C::THREADS>(st, kb, krs, t * C::BN, kvlim, tid);
+      dma_tile<D, C::BN, C::THREADS>(st + C::TILE, vb, krs, t * C::BN, kvlim, tid);
+    }
   };
   // Fill the ring before anything else so that the first tiles are on their
   // way while Q is loaded.

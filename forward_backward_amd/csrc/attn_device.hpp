@@ -168,6 +168,64 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long
   }
 }
 
+// Copy with a wave-uniform 64-bit base (scalar registers) and a per-lane
+// 32-bit byte offset: the address arithmetic is one scalar add per tile.
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory");
+}
+
+// Precomputed form of dma_tile for full tiles (every row valid): the lane
+// offsets (row * rs + swizzled chunk) are fixed at set-up, so each tile costs
+// one uniform base pointer. Needs (ROWS - 1) * rs * 2 + 2 * D < 2^32 bytes.
+template <int D, int ROWS, int THREADS>
+struct TileCopy {
+  static constexpr int RPW = 1024 / (2 * D);
+  static constexpr int CPR = D / 8;
+  static constexpr int WAVES = THREADS / 64;
+  static constexpr int ITERS = ROWS / (RPW * WAVES);
+  static_assert(ROWS % (RPW * WAVES) == 0, "tile rows must split evenly over the waves");
+  uint32_t voff[ITERS];  // byte offset of this lane's chunk from the tile's first row
+  uint32_t lds_wave;     // byte offset of this wave's first 1 KiB block in the tile (uniform)
+
+  __device__ __forceinline__ TileCopy(long rs, int tid) {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+      const int r = (i * WAVES + wave) * RPW + lane / CPR;
+      const int c = (lane % CPR) ^ swz_f<D>(r);
+      voff[i] = (uint32_t)((r * rs + c * 8) * 2);
+    }
+    lds_wave = __builtin_amdgcn_readfirstlane(wave * 1024);
+  }
+
+  // Rows [r0, r0 + ROWS) of g (row stride rs elements), all valid; g and r0
+  // wave-uniform.
+  __device__ __forceinline__ void copy(uint16_t* tile, const uint16_t* g, long rs, int r0) const {
+    const uint16_t* base = g + (long)r0 * rs;
+    const uint32_t l0 = lds_addr(tile) + lds_wave;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) dma16_s(base, voff[i], l0 + i * WAVES * 1024);
+  }
+
+  // Same through the compiler builtin (see dma_tile's VISIBLE).
+  __device__ __forceinline__ void copy_visible(uint16_t* tile, const uint16_t* g, long rs, int r0) const {
+    const char* base = (const char*)(g + (long)r0 * rs);
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(base + voff[i]),
+                                       (lds_void_t*)((char*)tile + lds_wave + i * WAVES * 1024), 16, 0, 0);
+  }
+};
+
 // Asynchronous copy of 64 consecutive floats (indices clamped to < lim, lim >= 1)
 // into LDS by one wave.
 __device__ __forceinline__ void dma_row64(float* dst, const float* g, int i0, int lim, int lane) {

@@ -17,13 +17,19 @@
 //   O^T += V^T P^T   (32x32x16 MFMA; P is converted from the S accumulator
 //                    registers directly, V is read with the LDS transpose read
 //                    so its key order matches the registers of P).
-// K/V tiles are double-buffered in LDS with a register prefetch of the next
-// tile's global loads. Keys at or past min(Tkv, kv_len[b]) and, with causal
-// masking, past the query tile are neither loaded nor computed; rows of a
-// partially valid tile are masked element-wise and out-of-range K/V rows are
-// zero-filled so that no stale value can reach the accumulators.
+// Software pipeline: while the matrix core computes S for tile j + 1, the
+// vector unit runs the softmax of tile j; then O += P_j V_j. K and V tiles
+// stream into two-stage LDS rings by direct global->LDS copies, K one tile
+// ahead of V: during iteration j the copies of K_{j+2} and V_{j+1} are in
+// flight while K_{j+1} and V_j are read. Tiles use the swizzled unpadded
+// layout of attn_device.hpp (no bank conflicts for row or transpose reads).
+// Keys at or past min(Tkv, kv_len[b]) and, with causal masking, past the
+// query tile are never read; rows of a partially valid tile are masked
+// element-wise (the copies of rows past the end repeat the last valid row).
 #include "attn_device.hpp"
 #include "attn_internal.h"
+
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -37,19 +43,13 @@ struct FwdCfg {
   static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;           // MFMA k-steps over head_dim
   static constexpr int DB = D / 32;           // 32-wide blocks of head_dim in O
-  static constexpr int KSTRIDE = D + 8;       // LDS row stride of K (elements)
-  static constexpr int VSTRIDE = D + 32;      // LDS row stride of V (elements)
-  static constexpr int KTILE = BN * KSTRIDE;
-  static constexpr int VTILE = BN * VSTRIDE;
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int CPT = BN * CPR / THREADS;  // chunks per thread per tile
-  static_assert(BN * CPR % THREADS == 0, "tile must split evenly over the workgroup");
+  static constexpr int TILE = BN * D;         // elements of one K or V tile
 };
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (C::KTILE + C::VTILE)];
+  __shared__ __attribute__((aligned(16))) uint16_t k_s0[C::TILE], k_s1[C::TILE], v_s0[C::TILE], v_s1[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,6 +76,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   if (a.causal) kv_end = min(kv_end, q0 + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
+  const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
+  auto issue_k = [&](int j, uint16_t* dst) {
+    if ((j + 1) * C::BN <= kv_end)
+      kvcopy.copy(dst, kb, krs, j * C::BN);
+    else
+      dma_tile<D, C::BN, C::THREADS>(dst, kb, krs, j * C::BN, kv_end, tid);
+  };
+  auto issue_v = [&](int j, uint16_t* dst) {
+    if ((j + 1) * C::BN <= kv_end)
+      kvcopy.copy(dst, vb, krs, j * C::BN);
+    else
+      dma_tile<D, C::BN, C::THREADS>(dst, vb, krs, j * C::BN, kv_end, tid);
+  };
+  if (ntiles > 0) {
+    issue_k(0, k_s0);
+    issue_v(0, v_s0);
+    if (ntiles > 1) issue_k(1, k_s1);
+  }
+
   const int qrow = q0 + 32 * wave + l32;
   const bool row_ok = qrow < a.Tq;
 
@@ -85,6 +104,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   for (int t = 0; t < C::KS; ++t) {
     qf[t] = row_ok ? gload16(qb + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
   }
+  // Take Q before the loop: the compiler cannot see the copies, and a first
+  // use of Q inside the loop would make it wait for all loads on every pass.
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) asm volatile("" ::"v"(qf[t]));
 
   f32x16_t o[C::DB];
 #pragma unroll
@@ -93,132 +116,147 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   float lsum = 0.f;      // this lane's share of the softmax denominator
 
   const float c = a.scale_log2;
-
-  u32x4_t kr[C::CPT], vr[C::CPT];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + C::THREADS * i;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      const int key = k0 + row;
-      if (key < kv_end) {
-        kr[i] = gload16(kb + key * krs + cc * 8);
-        vr[i] = gload16(vb + key * krs + cc * 8);
-      } else {
-        kr[i] = u32x4_t{0, 0, 0, 0};
-        vr[i] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* kl = lds + buf * (C::KTILE + C::VTILE);
-    uint16_t* vl = kl + C::KTILE;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int ch = tid + C::THREADS * i;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      lds_write16(kl + row * C::KSTRIDE + cc * 8, kr[i]);
-      lds_write16(vl + row * C::VSTRIDE + cc * 8, vr[i]);
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  // Transpose-read addressing of V (see attn_device.hpp): lane supplies the
-  // chunk of row (4*hh + (lane%16)/4) and columns 16*((lane/16)%2) + 4*(lane%4).
-  const int tr_row = 4 * hh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int wave_min_row = q0 + 32 * wave;
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = it * C::BN;
-    if (it + 1 < ntiles) gload(k0 + C::BN);
-    const uint16_t* kl = lds + (it & 1) * (C::KTILE + C::VTILE);
-    const uint16_t* vl = kl + C::KTILE;
+  // Swizzled LDS offsets of this lane's reads (row blocks of 16 keep the swizzle).
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int nrm[C::KS], trd[C::DB][2];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    trd[db][0] = swz_off<D>(tr_row, 32 * db + tr_col);
+    trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col);
+  }
 
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+  // S^T for the two 32-key blocks of a K tile.
+  auto sdot = [&](const uint16_t* kl, f32x16_t (&s)[2]) {
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
 #pragma unroll
-    for (int t = 0; t < C::KS; ++t) {
+    for (int t = 0; t < C::KS; ++t)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x4_t kf = lds_read16(kl + (32 * j + l32) * C::KSTRIDE + 16 * t + 8 * hh);
-        s[j] = mfma_bf16(kf, qf[t], s[j]);
-      }
-    }
+      for (int j = 0; j < 2; ++j) s[j] = mfma_bf16(lds_read16(kl + 32 * j * D + nrm[t]), qf[t], s[j]);
+  };
 
-    const bool need_mask = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
-    if (need_mask) {
+  // Softmax of tile j in place (S -> P, unnormalised) and the packed bf16
+  // B operands of the PV product. Returns whether O must be rescaled by
+  // `alpha` (wave-uniform); the rescale itself is left to the caller so that
+  // this stays free of branches.
+  auto softmax = [&](auto mask_tag, int j, f32x16_t (&s)[2], u32x4_t (&pf)[4], float& alpha) -> bool {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k0 = j * C::BN;
+    if constexpr (MASK) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int key = k0 + 32 * x + 8 * (r >> 2) + 4 * hh + (r & 3);
           const bool ok = key < kvlim && (!a.causal || key <= qrow);
-          s[j][r] = ok ? s[j][r] : -INFINITY;
+          s[x][r] = ok ? s[x][r] : -INFINITY;
         }
-      }
     }
-
     float mt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[j][r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[x][r]);
     mt = half_max(mt);
     // Lazy rescaling: the reference max m only moves when some row of the
     // wave would otherwise see exponentials above 2^kRescaleLog2 (or had no
     // valid key yet). Numerator and denominator share the reference, so the
     // result is the same; it only bounds P (kept <= 2^8, exact in bf16's range).
     const bool grow = (m == -INFINITY) ? (mt != -INFINITY) : ((mt - m) * c > kRescaleLog2);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float mnew = fmaxf(m, mt);
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mnew) * c);
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
-      m = mnew;
-    }
+    const bool any = __builtin_amdgcn_ballot_w64(grow) != 0;
+    const float mnew = any ? fmaxf(m, mt) : m;
+    alpha = (m == -INFINITY || !any) ? (m == -INFINITY ? 0.f : 1.f) : fast_exp2((m - mnew) * c);
+    m = mnew;
+    lsum *= alpha;
     const float nb = (m == -INFINITY) ? 0.f : -m * c;
     float ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[j][r], c, nb));
-        s[j][r] = p;
+        const float p = fast_exp2(__builtin_fmaf(s[x][r], c, nb));
+        s[x][r] = p;
         ps += p;
       }
     lsum += ps;
-
-    // P (bf16) as the B operand of O^T += V^T P^T, one operand per 16 keys.
-    u32x4_t pf[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r0 = 8 * u;
-        pf[2 * j + u] = u32x4_t{pack_bf16(s[j][r0 + 0], s[j][r0 + 1]), pack_bf16(s[j][r0 + 2], s[j][r0 + 3]),
-                                pack_bf16(s[j][r0 + 4], s[j][r0 + 5]), pack_bf16(s[j][r0 + 6], s[j][r0 + 7])};
+        pf[2 * x + u] = u32x4_t{pack_bf16(s[x][r0 + 0], s[x][r0 + 1]), pack_bf16(s[x][r0 + 2], s[x][r0 + 3]),
+                                pack_bf16(s[x][r0 + 4], s[x][r0 + 5]), pack_bf16(s[x][r0 + 6], s[x][r0 + 7])};
       }
+    return any;
+  };
 
+  auto pv = [&](const uint16_t* vl, const u32x4_t (&pf)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint16_t* vrow = vl + (16 * ks + tr_row) * C::VSTRIDE + tr_col;
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const u32x2_t lo = lds_read_tr(vrow + 32 * db);
-        const u32x2_t hi = lds_read_tr(vrow + 8 * C::VSTRIDE + 32 * db);
-        const u32x4_t vf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        o[db] = mfma_bf16(vf, pf[ks], o[db]);
+        const u32x2_t lo = lds_read_tr(vl + 16 * ks * D + trd[db][0]);
+        const u32x2_t hi = lds_read_tr(vl + 16 * ks * D + trd[db][1]);
+        o[db] = mfma_bf16(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[ks], o[db]);
       }
-    }
+  };
 
-    if (it + 1 < ntiles) lstore((it + 1) & 1);
+  f32x16_t s_cur[2], s_nxt[2];
+  if (ntiles > 0) {
+    wait_vmem();
     __syncthreads();
+    sdot(k_s0, s_cur);
+    __syncthreads();  // every wave has read K_0 before K_2 overwrites it
+  }
+
+  // Iteration j: copies of K_{j+2} and V_{j+1} start; S_{j+1} from K_{j+1}
+  // (on the last tile a stale stage whose result is dropped) runs beside the
+  // softmax of tile j; then O += P_j V_j.
+  auto step = [&](int j, const uint16_t* kn, uint16_t* kfree, const uint16_t* vc, uint16_t* vfree) {
+    if (j + 2 < ntiles) issue_k(j + 2, kfree);
+    if (j + 1 < ntiles) issue_v(j + 1, vfree);
+    const int k0 = j * C::BN;
+    const bool need_mask = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
+    u32x4_t pf[4];
+    float alpha;
+    bool any;
+    auto body = [&](auto mask_tag) {
+      sdot(kn, s_nxt);
+      any = softmax(mask_tag, j, s_cur, pf, alpha);
+#pragma unroll
+      for (int i = 0; i < 2 * C::KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then vector ALU work
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (need_mask)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+    if (any) {
+#pragma unroll
+      for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
+    }
+    pv(vc, pf);
+    s_cur[0] = s_nxt[0];
+    s_cur[1] = s_nxt[1];
+    wait_vmem();
+    __syncthreads();
+  };
+
+  // Stage roles alternate between iterations; unrolled by two so that every
+  // LDS address is a constant offset from the lane's base.
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, k_s1, k_s0, v_s0, v_s1);
+    if (j + 1 >= ntiles) break;
+    step(j + 1, k_s0, k_s1, v_s1, v_s0);
   }
 
   const float ltot = half_sum(lsum);
