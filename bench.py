@@ -63,6 +63,9 @@ def parse_args():
                          "the summaries under profiles/ and exit (no GPU use)")
     ap.add_argument("--profile-command", default="", help="kernel-trace command recorded in the summaries")
     ap.add_argument("--counter-command", default="", help="counter-pass command recorded in the summaries")
+    ap.add_argument("--mfma-dir", default="", help="with --summarize: rocprofv3 output of a pass with "
+                    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+    ap.add_argument("--mfma-command", default="", help="MFMA counter-pass command recorded in the summaries")
     return ap.parse_args()
 
 
@@ -201,6 +204,60 @@ def summarize(stats_dir, fetch_dir, write_dir, command, counter_command):
         json.dump({"source_digest": source_digest(), "command": counter_command,
                    "kernels": {k: {"bytes_per_launch": round(v)} for k, v in traffic.items()}}, f, indent=1)
     print(f"wrote summaries under {prof}")
+
+
+def summarize_mfma(stats_dir, mfma_dir, command, profile_command):
+    """MFMA utilisation per kernel at the clock the chip actually ran.
+
+    SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD's matrix unit;
+    GRBM_GUI_ACTIVE sums the GPU's active cycles over the 8 XCDs. Dividing the
+    latter by 8 and by the kernel's duration (kernel-trace average of the same
+    leg) gives the clock; busy / (cycles per XCD * 1024 SIMDs) is the fraction
+    of the matrix units' time spent on MFMAs, independent of the clock.
+    """
+    import csv
+    import glob
+    import re
+    w = int((re.search(r"--warmup (\d+)", profile_command or "") or [None, 3])[1])
+    k = int((re.search(r"--steps (\d+)", profile_command or "") or [None, 20])[1])
+    busy = _read_counter_csv(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    insts = _read_counter_csv(mfma_dir, "SQ_INSTS_MFMA")
+    grbm = _read_counter_csv(mfma_dir, "GRBM_GUI_ACTIVE")
+    durations = {}
+    for path in glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            durations[_short_name(r["Name"])] = float(r["AverageNs"])
+    # Durations of the headline leg (the kernel-trace average mixes in the causal leg).
+    trace = {}
+    for path in glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            trace.setdefault(_short_name(r["Kernel_Name"]), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    lines = ["# MFMA utilisation: attention fwd+bwd B4 H8 d128 T8192, non-causal", "",
+             "One rocprofv3 counter pass (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE) "
+             "of the command below. GRBM_GUI_ACTIVE sums active cycles over the 8 XCDs; divided by 8 and by the "
+             "kernel's headline-leg duration from the kernel trace it gives the clock the chip ran at. "
+             "`MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES / (cycles per XCD x 1024 SIMDs): the fraction of the matrix "
+             "units' time spent on MFMAs at that clock (the published peak assumes 2.4 GHz).", "",
+             "```", command or "", "```", "",
+             "| kernel | MFMA instructions | busy cycles per MFMA | cycles per XCD | duration us | clock GHz | "
+             "MFMA busy |", "|---|---|---|---|---|---|---|"]
+    for (name, grid), bv in sorted(busy.items()):
+        if not name.startswith("attn") or name not in trace:
+            continue
+        b = sum(bv) / len(bv)
+        if b == 0:
+            continue
+        n = sum(insts.get((name, grid), [0.0])) / max(len(insts.get((name, grid), [1])), 1)
+        g = sum(grbm.get((name, grid), [0.0])) / max(len(grbm.get((name, grid), [1])), 1)
+        head = sorted(d for _, d in sorted(trace[name])[w:w + k])  # timed steps of the headline leg
+        dur = head[len(head) // 2] / 1e3  # median, us
+        cyc = g / 8
+        lines.append(f"| `{name}` | {n:.4g} | {b / max(n, 1):.1f} | {cyc:.4g} | {dur:.1f} | "
+                     f"{cyc / (dur * 1e3):.2f} | {b / (cyc * 1024):.1%} |")
+    with open(os.path.join(ROOT, "profiles", "fwd_bwd_d128_T8192_mfma_util.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote MFMA utilisation summary")
 
 
 def device_tensors(case, seed=0, with_do=True):
@@ -356,6 +413,8 @@ def main():
     args = parse_args()
     if args.summarize:
         summarize(*args.summarize, args.profile_command, args.counter_command)
+        if args.mfma_dir:
+            summarize_mfma(args.summarize[0], args.mfma_dir, args.mfma_command, args.profile_command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
