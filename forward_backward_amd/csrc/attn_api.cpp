@@ -88,7 +88,7 @@ static size_t bwd_stat_bytes(const attn_params_t* p) {
 
 size_t attn_bwd_workspace_size(const attn_params_t* p) {
   if (p == nullptr) return 0;
-  return 2 * bwd_stat_bytes(p);
+  return 6 * bwd_stat_bytes(p);
 }
 
 attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -132,6 +132,7 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
   std::memset(&a, 0, sizeof(a));
   a.delta = static_cast<float*>(const_cast<void*>(ws));
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ws)) + bwd_stat_bytes(p));
+  a.rowstat = reinterpret_cast<uint16_t*>(static_cast<char*>(const_cast<void*>(ws)) + 2 * bwd_stat_bytes(p));
   a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;

@@ -32,42 +32,52 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ----------------------------------------------------------------- dK / dV
 //
 // One workgroup per (batch, KV head, 128 keys), 4 waves of 32 keys; K and V
-// rows of the wave's keys stay in registers as B operands. For each query
-// head of the group and each 64-row query tile, in a fixed order:
-//   S = Q K^T, dP = dO V^T       (lane = key, registers = query rows)
+// rows of the wave's keys stay in registers as B operands. The query rows of
+// the G heads of the group are visited in a fixed order, in 64-row tiles of
+// two 32-row blocks. Per block:
+//   S = Q K^T, dP = dO V^T        (lane = key, registers = query rows)
 //   P = exp2(S*c - LSE2), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS  (dO^T, Q^T by transpose reads)
-// The tile of four 32-row blocks is a software pipeline: block j+1's S/dP
-// products are interleaved with block j's softmax, so the vector work runs
-// under the matrix work.
+// The blocks form a three-deep software pipeline: step i issues the S/dP
+// products of block i and the dV/dK products of block i - 2 on the matrix
+// core while the vector unit runs the softmax of block i - 1, so every step
+// has the same 4*D/16 products to hide its vector work under. Tiles stream
+// through a three-stage LDS ring (a tile is read by four consecutive steps);
+// the copy of tile t + 2 starts once tile t - 1 has been read for the last
+// time. The pipeline runs one step before the first block and one after the
+// last on a zero-filled stage and on discarded results, so every step has
+// the same shape.
 
 template <int D>
 struct DkvCfg {
   static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave
   static constexpr int BM = 64;             // query rows per LDS tile
-  static constexpr int NB = BM / 32;        // 32-row blocks per tile (pipeline depth)
+  static constexpr int NST = 3;             // LDS stages
   static constexpr int THREADS = 256;
-  static constexpr int KS = D / 16;
+  static constexpr int KS = D / 16;         // k-steps of S and dP; also the dV/dK product pairs per block
   static constexpr int DB = D / 32;
+  static constexpr int EPS = 16 / KS;       // softmax elements per k-step
+  static constexpr int R = 2;               // depth of the fragment read-ahead (k-steps)
   static constexpr int TILE = BM * D;       // swizzled, unpadded (read row-wise and transposed)
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   using C = DkvCfg<D>;
-  // Two pipeline stages of the Q and dO tiles in one array, so that one
-  // per-lane offset plus a constant addresses every stage.
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * C::TILE];
-  __shared__ __attribute__((aligned(16))) float l_s0[C::BM], l_s1[C::BM];  // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float d_s0[C::BM], d_s1[C::BM];  // D = rowsum(dO * O)
-  uint16_t* const q_s0 = tiles;
-  uint16_t* const g_s0 = tiles + C::TILE;   // dO tiles
-  uint16_t* const q_s1 = tiles + 2 * C::TILE;
-  uint16_t* const g_s1 = tiles + 3 * C::TILE;
+  // One LDS array: [row-term stages | Q stages | dO stages], so that every
+  // read is a lane register plus an immediate below 64 KiB.
+  constexpr int TB = C::TILE * 2;                 // bytes of one tile
+  constexpr int R_OFF = 0;                        // row terms: 16 bytes per query row
+  constexpr int Q_OFF = C::NST * C::BM * 16;      // Q stages
+  constexpr int G_OFF = Q_OFF + C::NST * TB;      // dO stages
+  __shared__ __attribute__((aligned(16))) char smem[G_OFF + C::NST * TB];
+  uint16_t* const q_st = (uint16_t*)(smem + Q_OFF);
+  uint16_t* const g_st = (uint16_t*)(smem + G_OFF);
+  uint16_t* const r_st = (uint16_t*)(smem + R_OFF);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
@@ -92,7 +102,12 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
     dv[i] = f32x16_t{};
   }
 
-  if (k0 < kvlim) {
+  const int qt_begin = a.causal ? k0 / C::BM : 0;
+  const int nqt = (a.Tq + C::BM - 1) / C::BM;
+  const int nq = nqt - qt_begin;
+  const int ntiles = G * nq;  // (query head, query tile) pairs in a fixed order
+
+  if (k0 < kvlim && ntiles > 0) {
     // K and V rows of this lane's key as B operands (k = head_dim).
     u32x4_t kf[C::KS], vf[C::KS];
     const bool key_ok = key < kvlim;
@@ -104,29 +119,38 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
     const float c = a.scale_log2;
     const int tr_row = 4 * hh + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int wave_min_key = k0 + 32 * wave;
-    const int wave_max_key = wave_min_key + 31;
-    const int qt_begin = a.causal ? k0 / C::BM : 0;
-    const int nqt = (a.Tq + C::BM - 1) / C::BM;
-    const int nq = nqt - qt_begin;
-    const int ntiles = G * nq;  // (query head, query tile) pairs in a fixed order
+    const int wave_max_key = k0 + 32 * wave + 31;
 
-    // Per-lane swizzled offsets (elements); the row block and stage parts are
-    // compile-time constants (swz_f depends only on the low 4 bits of the row).
-    int nrm[C::KS], trd[C::DB][2];
+    // Byte offsets of this lane's reads inside a tile (swizzled layout).
+    uint32_t row_off[C::KS], tr_off[C::DB][2];
 #pragma unroll
-    for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
+    for (int t = 0; t < C::KS; ++t) row_off[t] = 2 * swz_off<D>(l32, 16 * t + 8 * hh);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-      trd[db][0] = swz_off<D>(tr_row, 32 * db + tr_col);
-      trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col);
+      tr_off[db][0] = 2 * swz_off<D>(tr_row, 32 * db + tr_col);
+      tr_off[db][1] = 2 * swz_off<D>(tr_row + 8, 32 * db + tr_col);
+    }
+
+    // The stage of "tile -1" (the last one) starts as zeros: the two steps
+    // before the first block compute with it, and zeros add nothing.
+    {
+      constexpr int ZS = C::NST - 1;
+      const u32x4_t z = {0, 0, 0, 0};
+      for (int e = tid * 8; e < C::TILE; e += C::THREADS * 8) {
+        lds_write16(q_st + ZS * C::TILE + e, z);
+        lds_write16(g_st + ZS * C::TILE + e, z);
+      }
+      if (tid < C::BM) lds_write16(r_st + (ZS * C::BM + tid) * 8, z);
     }
 
     const TileCopy<D, C::BM, C::THREADS> qcopy(qrs, tid);
-    auto issue = [&](int idx, uint16_t* qs, uint16_t* gs, float* ls, float* ds) {
-      const int h = kh * G + idx / nq;
-      const int q0 = (qt_begin + idx % nq) * C::BM;
+    auto tile_q0 = [&](int t) { return (qt_begin + t % nq) * C::BM; };
+    auto issue = [&](int t, int st) {
+      const int h = kh * G + t / nq;
+      const int q0 = tile_q0(t);
       const long hoff = ((long)b * a.Tq * a.Hq + h) * D;
+      uint16_t* qs = q_st + st * C::TILE;
+      uint16_t* gs = g_st + st * C::TILE;
       if (q0 + C::BM <= a.Tq) {
         qcopy.copy(qs, (const uint16_t*)a.q + hoff, qrs, q0);
         qcopy.copy(gs, (const uint16_t*)a.dout + hoff, qrs, q0);
@@ -134,152 +158,169 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
         dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
         dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
       }
-      const long stat0 = ((long)b * a.Hq + h) * a.Tq;
-      static_assert(C::BM == 64, "row statistics are copied by two waves of 64 lanes");
-      if (wave == 0) dma_row64(ls, a.lse2 + stat0, q0, a.Tq, lane);
-      if (wave == 1) dma_row64(ds, a.delta + stat0, q0, a.Tq, lane);
-    };
-
-    // S = Q K^T and dP = dO V^T of block qb, with the row fragments read
-    // through a two-deep register ring (the reads of step t + 2 are issued as
-    // soon as the products of step t have taken their operands).
-    auto sdp = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, f32x16_t& s, f32x16_t& dp) {
-      const uint16_t* qrow = qsb + 32 * qb * D;
-      const uint16_t* grow = gsb + 32 * qb * D;
-      u32x4_t qa[2], ga[2];
-      qa[0] = lds_read16(qrow + nrm[0]);
-      ga[0] = lds_read16(grow + nrm[0]);
-      qa[1] = lds_read16(qrow + nrm[1]);
-      ga[1] = lds_read16(grow + nrm[1]);
-      s = f32x16_t{};
-      dp = f32x16_t{};
-#pragma unroll
-      for (int t = 0; t < C::KS; ++t) {
-        s = mfma_bf16(qa[t & 1], kf[t], s);
-        dp = mfma_bf16(ga[t & 1], vf[t], dp);
-        if (t + 2 < C::KS) {
-          qa[t & 1] = lds_read16(qrow + nrm[t + 2]);
-          ga[t & 1] = lds_read16(grow + nrm[t + 2]);
-        }
+      // Row terms: one 16-byte row per lane of wave 0 (rows past Tq repeat
+      // the last row; their elements are masked).
+      static_assert(C::BM == 64, "row terms are copied by one wave of 64 lanes");
+      if (wave == 0) {
+        int i = q0 + lane;
+        i = i < a.Tq ? i : a.Tq - 1;
+        dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
       }
     };
-    // P and dS of block qb as bf16 B operands (16 query rows each).
-    auto softmax = [&](auto mask_tag, const float* ls, const float* ds, int q0, int qb, const f32x16_t& s,
-                       const f32x16_t& dp, u32x4_t* pb, u32x4_t* dsb) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      f32x4_t lv[4], dl[4];
+    // Whether tile t needs the element-wise mask (key or causal bound inside
+    // the wave's keys, or a ragged last query tile). The pipeline's extra
+    // tiles (t < 0, t >= ntiles) compute on zeros or are discarded.
+    auto mask_tile = [&](int t) {
+      if (t < 0 || t >= ntiles) return false;
+      const int q0 = tile_q0(t);
+      return (wave_max_key >= kvlim) || (a.causal && q0 < wave_max_key) || (q0 + C::BM > a.Tq);
+    };
+
+    // Pipeline registers: S/dP accumulators and the packed P/dS operands,
+    // two sets each (set = block parity).
+    f32x16_t sacc[2], pacc[2];
+    u32x4_t pk_p[2][2], pk_d[2][2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lv[g] = *(const f32x4_t*)(ls + 32 * qb + 8 * g + 4 * hh);
-        dl[g] = *(const f32x4_t*)(ds + 32 * qb + 8 * g + 4 * hh);
+    for (int x = 0; x < 2; ++x) {
+      sacc[x] = f32x16_t{};
+      pacc[x] = f32x16_t{};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pk_p[x][u] = u32x4_t{0, 0, 0, 0};
+        pk_d[x][u] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+
+    // Lane byte offsets of the current pair of steps: row reads go to the
+    // stage of tile p, transpose reads to the stage of tile p - 1.
+    uint32_t rcur[C::KS], tprev[C::DB][2];
+
+    // Row terms enter S and dP through one extra k-step each: the A operand
+    // is the query row's 16 bytes of terms (-LSE/scale in elements 0..2, -D in
+    // 4..6, read by both lane halves), the B operand selects them with ones in
+    // the first lane half (k = 0..7): S' = S - LSE/scale, dP' = dP - D, so
+    // that P = exp2(c * S') and dS = P * dP'.
+    const unsigned one2 = 0x3F803F80u, one1 = 0x00003F80u;
+    const u32x4_t sel_s = hh == 0 ? u32x4_t{one2, one1, 0, 0} : u32x4_t{0, 0, 0, 0};
+    const u32x4_t sel_d = hh == 0 ? u32x4_t{0, 0, one2, one1} : u32x4_t{0, 0, 0, 0};
+
+    // One pipeline step: RB is the 32-row block of tile p whose S/dP are
+    // formed (into accumulator set RB); the softmax takes block 1 - RB of
+    // tile p - 1 (RB = 0) or block 0 of tile p (RB = 1) from set 1 - RB; the
+    // dV/dK products take block RB of tile p - 1 (transposed) with packed set
+    // RB. `rterm` is this lane's row-term offset (bytes) for block RB.
+    auto step = [&](auto rb_, bool mask, int q0m, uint32_t rterm) {
+      constexpr int RB = decltype(rb_)::value;
+      constexpr int A = RB;        // accumulator set written by this step
+      constexpr int P = 1 - RB;    // set read by the softmax
+      constexpr int SB = 1 - RB;   // block of the softmax's rows within its tile
+      u32x4_t qa[C::R], ga[C::R];
+      u32x2_t tg[C::R][2], tx[C::R][2];
+      auto read_rows = [&](int m, int slot) {
+        qa[slot] = lds_read16((const uint16_t*)(smem + rcur[m] + Q_OFF + 32 * RB * D * 2));
+        ga[slot] = lds_read16((const uint16_t*)(smem + rcur[m] + G_OFF + 32 * RB * D * 2));
+      };
+      // Transposed operands of dV/dK product pair m: half u = m / DB (16
+      // query rows), head_dim block db = m % DB.
+      auto read_tr = [&](int m, int slot) {
+        const int u = m / C::DB, db = m % C::DB;
+        const int boff = (32 * RB + 16 * u) * D * 2;
+        tg[slot][0] = lds_read_tr((const uint16_t*)(smem + tprev[db][0] + G_OFF + boff));
+        tg[slot][1] = lds_read_tr((const uint16_t*)(smem + tprev[db][1] + G_OFF + boff));
+        tx[slot][0] = lds_read_tr((const uint16_t*)(smem + tprev[db][0] + Q_OFF + boff));
+        tx[slot][1] = lds_read_tr((const uint16_t*)(smem + tprev[db][1] + Q_OFF + boff));
+      };
+#pragma unroll
+      for (int m = 0; m < C::R; ++m) {
+        read_rows(m, m);
+        read_tr(m, m);
+      }
+      f32x16_t& s = sacc[A];
+      f32x16_t& dp = pacc[A];
+      s = f32x16_t{};
+      dp = f32x16_t{};
+      const f32x16_t& sin = sacc[P];
+      const f32x16_t& din = pacc[P];
+      const u32x4_t terms = lds_read16((const uint16_t*)(smem + rterm));
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int m = 0; m < C::KS; ++m) {
+        const int slot = m % C::R;
+        s = mfma_bf16(qa[slot], kf[m], s);
+        dp = mfma_bf16(ga[slot], vf[m], dp);
+        {
+          const int u = m / C::DB, db = m % C::DB;
+          dv[db] = mfma_bf16(u32x4_t{tg[slot][0][0], tg[slot][0][1], tg[slot][1][0], tg[slot][1][1]}, pk_p[A][u],
+                             dv[db]);
+          dk[db] = mfma_bf16(u32x4_t{tx[slot][0][0], tx[slot][0][1], tx[slot][1][0], tx[slot][1][1]}, pk_d[A][u],
+                             dk[db]);
+        }
+        if (m + C::R < C::KS) {
+          read_rows(m + C::R, slot);
+          read_tr(m + C::R, slot);
+        }
+        if (m == C::KS - 1) {
+          s = mfma_bf16(terms, sel_s, s);
+          dp = mfma_bf16(terms, sel_d, dp);
+        }
+#pragma unroll
+        for (int e = 0; e < C::EPS; ++e) {
+          const int r = C::EPS * m + e;
+          const float p = fast_exp2(sin[r] * c);
+          pv[r] = p;
+          dsv[r] = p * din[r];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Element-wise mask, only on tiles that cross a key, causal or row
+      // bound. A select (not a product) so that the non-finite values of
+      // invalid elements cannot leak.
+      if (mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = q0m + 32 * SB + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool ok = (key < kvlim) & (!a.causal | (key <= ql)) & (ql < a.Tq);
+          pv[r] = ok ? pv[r] : 0.f;
+          dsv[r] = ok ? dsv[r] : 0.f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        float pv[8], dsv[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int r = 8 * u + x;
-          float p = fast_exp2(__builtin_fmaf(s[r], c, -lv[r >> 2][r & 3]));
-          if constexpr (MASK) {
-            const int ql = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = (key < kvlim) & (!a.causal | (key <= ql)) & (ql < a.Tq);
-            p = ok ? p : 0.f;
-          }
-          pv[x] = p;
-          dsv[x] = p * (dp[r] - dl[r >> 2][r & 3]);
-        }
-        pb[u] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                        pack_bf16(pv[6], pv[7])};
-        dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                         pack_bf16(dsv[6], dsv[7])};
-      }
-    };
-    // dV^T += dO^T P and dK^T += Q^T dS for half u (16 query rows) of block qb:
-    // transpose reads of dO and Q, then the products.
-    struct TrFrags {
-      u32x2_t g[C::DB][2], x[C::DB][2];
-    };
-    auto read_tr = [&](const uint16_t* qsb, const uint16_t* gsb, int qb, int u, TrFrags& f) {
-      const uint16_t* gblk = gsb + (32 * qb + 16 * u) * D;
-      const uint16_t* qblk = qsb + (32 * qb + 16 * u) * D;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        f.g[db][0] = lds_read_tr(gblk + trd[db][0]);
-        f.g[db][1] = lds_read_tr(gblk + trd[db][1]);
-        f.x[db][0] = lds_read_tr(qblk + trd[db][0]);
-        f.x[db][1] = lds_read_tr(qblk + trd[db][1]);
-      }
-    };
-    auto dvdk_half = [&](const TrFrags& f, const u32x4_t& p, const u32x4_t& dsv) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        dv[db] = mfma_bf16(u32x4_t{f.g[db][0][0], f.g[db][0][1], f.g[db][1][0], f.g[db][1][1]}, p, dv[db]);
-        dk[db] = mfma_bf16(u32x4_t{f.x[db][0][0], f.x[db][0][1], f.x[db][1][0], f.x[db][1][1]}, dsv, dk[db]);
+        pk_p[P][u] = u32x4_t{pack_bf16(pv[8 * u + 0], pv[8 * u + 1]), pack_bf16(pv[8 * u + 2], pv[8 * u + 3]),
+                             pack_bf16(pv[8 * u + 4], pv[8 * u + 5]), pack_bf16(pv[8 * u + 6], pv[8 * u + 7])};
+        pk_d[P][u] = u32x4_t{pack_bf16(dsv[8 * u + 0], dsv[8 * u + 1]), pack_bf16(dsv[8 * u + 2], dsv[8 * u + 3]),
+                             pack_bf16(dsv[8 * u + 4], dsv[8 * u + 5]), pack_bf16(dsv[8 * u + 6], dsv[8 * u + 7])};
       }
     };
 
-    // One query tile from stage (qsb, gsb, ls, ds); the next tile's loads into
-    // the other stage start at the top.
-    auto tile = [&](int idx, const uint16_t* qsb, const uint16_t* gsb, const float* ls, const float* ds,
-                    auto&& issue_next) {
-      const int q0 = (qt_begin + idx % nq) * C::BM;
-      issue_next();
-      const bool mask_tile =
-          (wave_max_key >= kvlim) || (a.causal && q0 < wave_max_key) || (q0 + C::BM > a.Tq);
-      // Pipeline over the two 32-row blocks:
-      //   S/dP(0);  [S/dP(1) | softmax(0)];  [dV/dK(0) | softmax(1)];  dV/dK(1)
-      // where [x | y] interleaves the products x with the vector work y.
-      auto body = [&](auto mask_tag) {
-        f32x16_t s0, dp0, s1, dp1;
-        u32x4_t pb0[2], ds0[2], pb1[2], ds1[2];
-        TrFrags tf;
-        sdp(qsb, gsb, 0, s0, dp0);
-        __builtin_amdgcn_sched_barrier(0);
-        sdp(qsb, gsb, 1, s1, dp1);
-        softmax(mask_tag, ls, ds, q0, 0, s0, dp0, pb0, ds0);
-#pragma unroll
-        for (int i = 0; i < 2 * C::KS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then vector ALU work
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        read_tr(qsb, gsb, 0, 0, tf);
-        __builtin_amdgcn_sched_barrier(0);
-        dvdk_half(tf, pb0[0], ds0[0]);
-        read_tr(qsb, gsb, 0, 1, tf);
-        softmax(mask_tag, ls, ds, q0, 1, s1, dp1, pb1, ds1);
-        for (int i = 0; i < 2 * C::DB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transpose reads
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then vector ALU work
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        dvdk_half(tf, pb0[1], ds0[1]);
-        read_tr(qsb, gsb, 1, 0, tf);
-        dvdk_half(tf, pb1[0], ds1[0]);
-        read_tr(qsb, gsb, 1, 1, tf);
-        dvdk_half(tf, pb1[1], ds1[1]);
-      };
-      if (mask_tile)
-        body(std::true_type{});
-      else
-        body(std::false_type{});
-      wait_vmem();
-      __syncthreads();
-    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 
-    if (ntiles > 0) issue(0, q_s0, g_s0, l_s0, d_s0);
+    issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
     wait_vmem();
     __syncthreads();
-    for (int idx = 0; idx < ntiles; idx += 2) {
-      tile(idx, q_s0, g_s0, l_s0, d_s0, [&]() {
-        if (idx + 1 < ntiles) issue(idx + 1, q_s1, g_s1, l_s1, d_s1);
-      });
-      if (idx + 1 >= ntiles) break;
-      tile(idx + 1, q_s1, g_s1, l_s1, d_s1, [&]() {
-        if (idx + 2 < ntiles) issue(idx + 2, q_s0, g_s0, l_s0, d_s0);
-      });
+    // Steps 2p and 2p + 1 (tile p in stage p % 3, tile p - 1 in the stage
+    // before), then the ring advances: tile p + 1 must have landed and tile
+    // p - 1 is free for tile p + 2. One pair past the last tile drains the
+    // pipeline.
+    int scur = 0;
+    for (int p = 0; p <= ntiles; ++p) {
+      const int sprev = scur == 0 ? C::NST - 1 : scur - 1;
+#pragma unroll
+      for (int t = 0; t < C::KS; ++t) rcur[t] = row_off[t] + scur * TB;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        tprev[db][0] = tr_off[db][0] + sprev * TB;
+        tprev[db][1] = tr_off[db][1] + sprev * TB;
+      }
+      const uint32_t rterm = R_OFF + (scur * C::BM + l32) * 16;
+      step(I0{}, mask_tile(p - 1), tile_q0(p - 1 < 0 ? 0 : p - 1), rterm);
+      step(I1{}, mask_tile(p), tile_q0(p), rterm + 32 * 16);
+      wait_vmem();
+      __syncthreads();
+      if (p + 2 < ntiles) issue(p + 2, sprev);
+      scur = scur == C::NST - 1 ? 0 : scur + 1;
     }
   }
 

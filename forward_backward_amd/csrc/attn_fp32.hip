@@ -170,8 +170,23 @@ __global__ __launch_bounds__(64) void attn_dkdv_fp32_kernel(BwdArgs a) {
   }
 }
 
-// D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32, and the
-// base-2 LSE (LSE * log2(e)) that the tile kernels load straight into LDS.
+// Three bf16 terms whose sum is x to fp32 precision (each term is the
+// round-to-nearest-even bf16 of what the previous ones left; every
+// difference is exact in fp32).
+__device__ __forceinline__ u32x2_t split_bf16x3(float x) {
+  const float h = bf16_lo(pack_bf16(x, 0.f));
+  const float r1 = x - h;
+  const float m = bf16_lo(pack_bf16(r1, 0.f));
+  const float r2 = r1 - m;
+  return u32x2_t{pack_bf16(h, m), pack_bf16(r2, 0.f)};
+}
+
+// D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32, the base-2 LSE
+// (LSE * log2(e)) that the tile kernels load straight into LDS, and the row
+// terms the dK/dV kernel adds to S and dP with one extra matrix k-step:
+// -LSE/scale (so that scale * log2(e) * (S - LSE/scale) is the base-2
+// exponent of P) and -D, each as three bf16 terms. Rows without a finite LSE
+// (no valid key) get 0; no kernel forms P for them.
 // Each thread reduces 8 contiguous elements; D/8 threads share a row.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void attn_delta_kernel(BwdArgs a, long rows) {
@@ -205,7 +220,11 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(BwdArgs a, long rows) {
     const int b = (int)(row / ((long)a.Hq * a.Tq));
     const long st = ((long)b * a.Hq + h) * a.Tq + i;
     a.delta[st] = acc;
-    a.lse2[st] = a.lse[st] * 1.4426950408889634f;
+    const float lse = a.lse[st];
+    a.lse2[st] = lse * 1.4426950408889634f;
+    const float x = __builtin_isfinite(lse) ? -lse / a.scale : 0.f;
+    const u32x2_t xs = split_bf16x3(x), ys = split_bf16x3(-acc);
+    *(u32x4_t*)(a.rowstat + st * 8) = u32x4_t{xs[0], xs[1], ys[0], ys[1]};
   }
 }
 

@@ -35,6 +35,8 @@ struct BwdArgs {
   void* dv;
   float* delta;            // workspace: D = rowsum(dO * O), [B, Hq, Tq]
   float* lse2;             // workspace: LSE * log2(e), [B, Hq, Tq]
+  uint16_t* rowstat;       // workspace: [B, Hq, Tq][8] bf16, -LSE/scale and -D, each split into three
+                           // bf16 terms: (x_hi, x_mid, x_lo, 0, y_hi, y_mid, y_lo, 0)
   const int32_t* kv_lens;
   int B, Tq, Tkv, Hq, Hkv;
   float scale;

@@ -82,8 +82,10 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op);
 attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o,
                        float* lse, void* stream);
 
-/* Bytes of device workspace attn_bwd needs: two fp32 [B, Hq, Tq] row
- * statistics, D = rowsum(dO * O) and LSE * log2(e). */
+/* Bytes of device workspace attn_bwd needs: per query row (B * Hq * Tq rows)
+ * 24 bytes, each region rounded up to 256 bytes: D = rowsum(dO * O) and
+ * LSE * log2(e) (fp32 each), and 16 bytes of bf16 terms of -LSE/scale and -D
+ * that the dK/dV pass adds to its products. */
 size_t attn_bwd_workspace_size(const attn_params_t* p);
 
 /* Backward: deterministic two-pass scheme without atomics. A pre-kernel

@@ -85,7 +85,8 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.attn_fwd(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == attn.ATTN_ERR_INVALID
     args = [FAKE] * 9
     need = L.attn_bwd_workspace_size(ctypes.byref(p))
-    assert need == 2 * (2 * 8 * 128 * 4)
+    # D and LSE * log2(e) (fp32 each) and 16 bytes of bf16 row terms per query row
+    assert need == 6 * (2 * 8 * 128 * 4)
     assert L.attn_bwd(ctypes.byref(p), *args, None, 0, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), *args, FAKE, need - 1, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), None, *args[1:], FAKE, need, None) == attn.ATTN_ERR_INVALID
