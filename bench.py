@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the causal and decode legs")
     ap.add_argument("--decode-calls", type=int, default=200)
+    ap.add_argument("--suites", action="store_true",
+                    help="also time the GQA suite (fwd+bwd, native GQA against repeated K/V) and the decode suite")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of this many MiB (reference dispatch for HBM counters)")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -372,6 +374,133 @@ def time_decode(case, calls, sets=4):
     return replay, cold, warm, [int(x) for x in host["kv_lens"]]
 
 
+def device_normal(shape, seed):
+    """Seeded N(0,1) bf16 tensor drawn on the device (timing legs only; no oracle reads it)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
+
+
+def _time_steps(q, k, v, do, case, steps, warmup):
+    """ms per fwd+bwd step on given tensors; returns (ms, peak bytes allocated beyond the inputs)."""
+    import torch
+    from forward_backward_amd import attn
+
+    kw = dict(scale=case.scale, causal=case.causal)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    def step():
+        o, lse = attn.fwd(q, k, v, **kw)
+        return attn.bwd(q, k, v, o, lse, do, **kw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, peak
+
+
+def gqa_suite(steps):
+    """The pages' GQA suite: 32 query heads over 8 KV heads, head_dim 128, batch 1, Lq = Lkv = T.
+
+    Times fwd+bwd with native GQA (query head h reads KV head h // G) and the
+    same problem run as plain multi-head attention on K/V repeated G times
+    (dK/dV summed over each group afterwards), and reports the peak device
+    memory of each beyond the inputs.
+    """
+    import torch
+    from forward_backward_amd.inputs import workload_cases
+    from forward_backward_amd.metrics import attention_flops
+
+    rows = []
+    for case in workload_cases(5):
+        G = case.Hq // case.Hkv
+        q = device_normal((case.B, case.Tq, case.Hq, case.D), 1)
+        k = device_normal((case.B, case.Tkv, case.Hkv, case.D), 2)
+        v = device_normal((case.B, case.Tkv, case.Hkv, case.D), 3)
+        do = device_normal((case.B, case.Tq, case.Hq, case.D), 4)
+        ms, peak = _time_steps(q, k, v, do, case, steps, 2)
+
+        def repeated():
+            kr = k.repeat_interleave(G, dim=2)
+            vr = v.repeat_interleave(G, dim=2)
+            from forward_backward_amd import attn
+            o, lse = attn.fwd(q, kr, vr, scale=case.scale)
+            dq, dkr, dvr = attn.bwd(q, kr, vr, o, lse, do, scale=case.scale)
+            sh = (case.B, case.Tkv, case.Hkv, G, case.D)
+            return dq, dkr.view(sh).float().sum(3).to(torch.bfloat16), dvr.view(sh).float().sum(3).to(torch.bfloat16)
+
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        repeated()
+        torch.cuda.synchronize()
+        peak_rep = torch.cuda.max_memory_allocated() - base
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            repeated()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_rep = e0.elapsed_time(e1) / steps
+        fl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, case.causal, "fwd_bwd")
+        row = {"T": case.Tq, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+               "peak_mb": round(peak / 2**20, 1), "repeated_ms": round(ms_rep, 4),
+               "repeated_peak_mb": round(peak_rep / 2**20, 1)}
+        rows.append(row)
+        log(f"  gqa T{case.Tq}: {ms:.3f} ms ({row['tflops']} TFLOP/s), peak {row['peak_mb']} MB; "
+            f"repeated K/V {ms_rep:.3f} ms, peak {row['repeated_peak_mb']} MB")
+        del q, k, v, do
+    return {"shape": "bf16 B1 Hq32 Hkv8 d128 Lq=Lkv=T non-causal, fwd+bwd", "rows": rows}
+
+
+def decode_suite(calls):
+    """The pages' decode suite: one query per sequence, 32 query heads, head_dim 128, 8 or 32 KV heads.
+
+    Full caches (no length mask). Each call's caches rotate over enough copies
+    (>= 768 MiB in total) that they do not stay in the chip's last-level cache.
+    """
+    import math
+    import torch
+    from forward_backward_amd import attn
+    from forward_backward_amd.inputs import workload_cases
+    from forward_backward_amd.metrics import decode_bytes
+
+    rows = []
+    for case in workload_cases(6):
+        kv_bytes = 2 * case.B * case.Tkv * case.Hkv * case.D * 2
+        sets = max(1, min(16, math.ceil((768 << 20) / kv_bytes)))
+        q = device_normal((case.B, case.Tq, case.Hq, case.D), 1)
+        caches = [(device_normal((case.B, case.Tkv, case.Hkv, case.D), 2 + 2 * i),
+                   device_normal((case.B, case.Tkv, case.Hkv, case.D), 3 + 2 * i)) for i in range(sets)]
+        for i in range(2):
+            attn.decode(q, *caches[i % sets], scale=case.scale)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            attn.decode(q, *caches[i % sets], scale=case.scale)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / calls * 1e3
+        nbytes = decode_bytes(case.B, case.Tq, case.Hq, case.Hkv, case.D, [case.Tkv] * case.B)
+        row = {"B": case.B, "keys": case.Tkv, "Hkv": case.Hkv, "us_per_call": round(us, 2),
+               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes_per_call": nbytes, "cache_copies": sets}
+        rows.append(row)
+        log(f"  decode B{case.B} keys {case.Tkv} Hkv{case.Hkv}: {us:.1f} us/call, {row['gbs']} GB/s")
+        del q, caches
+    return {"shape": "bf16 Tq=1 Hq32 d128, full caches, eager calls", "rows": rows}
+
+
 def cpu_baseline(case, seconds):
     """The float64 oracle on a bounded sample: whole (batch, KV head) groups of the headline workload."""
     import numpy as np
@@ -489,6 +618,12 @@ def main():
         }
         log(f"decode {graph_ms * 1e3:.1f} us/call in a graph ({gbs:.0f} GB/s); eager {cold * 1e3:.1f} us, "
             f"same cache {warm * 1e3:.1f} us")
+
+    if args.suites:
+        log("GQA suite")
+        extra["gqa_suite"] = gqa_suite(max(2, min(args.steps, 5)))
+        log("decode suite")
+        extra["decode_suite"] = decode_suite(50)
 
     cpu = None
     if not args.no_cpu_baseline:

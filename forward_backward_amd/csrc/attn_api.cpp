@@ -86,9 +86,35 @@ static size_t bwd_stat_bytes(const attn_params_t* p) {
                   256);
 }
 
+// Query-head split of the bf16 dK/dV pass. One workgroup per (batch, KV
+// head, 128 keys) sums the gradients of all G query heads of the group; when
+// that leaves compute units idle (fewer than kBwdFillTarget workgroups), the G
+// heads are divided over S workgroups per KV tile that write fp32 partial
+// sums, and a reduction adds the S partials in a fixed order. A pure function
+// of the shape, so reruns are bitwise identical.
+static int bwd_kv_split(const attn_params_t* p, int* heads_per_split) {
+  const int G = (p->Hkv > 0 && p->Hq >= p->Hkv) ? p->Hq / p->Hkv : 1;
+  *heads_per_split = G;
+  if (p->dtype != ATTN_BF16 || G <= 1 || p->B <= 0 || p->Tkv <= 0) return 1;
+  const long base = (long)p->B * p->Hkv * ((p->Tkv + attn::kBwdBlockN - 1) / attn::kBwdBlockN);
+  if (base >= attn::kBwdFillTarget) return 1;
+  const long want = (attn::kBwdFillTarget + base - 1) / base;
+  const int s = (int)(want < G ? want : G);
+  const int hps = (G + s - 1) / s;
+  *heads_per_split = hps;
+  return (G + hps - 1) / hps;
+}
+
+static size_t bwd_part_bytes(const attn_params_t* p) {
+  int hps;
+  const int s = bwd_kv_split(p, &hps);
+  if (s <= 1) return 0;
+  return round_up(2 * (size_t)s * p->B * p->Tkv * p->Hkv * p->D * sizeof(float), 256);
+}
+
 size_t attn_bwd_workspace_size(const attn_params_t* p) {
   if (p == nullptr) return 0;
-  return 6 * bwd_stat_bytes(p);
+  return 6 * bwd_stat_bytes(p) + bwd_part_bytes(p);
 }
 
 attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -133,6 +159,10 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
   a.delta = static_cast<float*>(const_cast<void*>(ws));
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ws)) + bwd_stat_bytes(p));
   a.rowstat = reinterpret_cast<uint16_t*>(static_cast<char*>(const_cast<void*>(ws)) + 2 * bwd_stat_bytes(p));
+  a.kv_split = bwd_kv_split(p, &a.heads_per_split);
+  a.dkv_part = a.kv_split > 1
+                   ? reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ws)) + 6 * bwd_stat_bytes(p))
+                   : nullptr;
   a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;

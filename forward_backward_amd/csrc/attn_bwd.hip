@@ -83,10 +83,14 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = bid % a.num_ktiles;
-  const int bkh = bid / a.num_ktiles;
-  const int kh = bkh % a.Hkv;
-  const int b = bkh / a.Hkv;
+  int rest = bid / a.num_ktiles;
+  const int kh = rest % a.Hkv;
+  rest /= a.Hkv;
+  const int b = rest % a.B;
+  const int split = rest / a.B;              // which share of the group's query heads
   const int G = a.Hq / a.Hkv;
+  const int h_lo = split * a.heads_per_split;
+  const int nh = min(a.heads_per_split, G - h_lo);
   const int k0 = kt * C::BN;
   const int key = k0 + 32 * wave + l32;      // this lane's key
 
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   const int qt_begin = a.causal ? k0 / C::BM : 0;
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const int nq = nqt - qt_begin;
-  const int ntiles = G * nq;  // (query head, query tile) pairs in a fixed order
+  const int ntiles = nh * nq;  // (query head, query tile) pairs in a fixed order
 
   if (k0 < kvlim && ntiles > 0) {
     // K and V rows of this lane's key as B operands (k = head_dim).
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
     const TileCopy<D, C::BM, C::THREADS> qcopy(qrs, tid);
     auto tile_q0 = [&](int t) { return (qt_begin + t % nq) * C::BM; };
     auto issue = [&](int t, int st) {
-      const int h = kh * G + t / nq;
+      const int h = kh * G + h_lo + t / nq;
       const int q0 = tile_q0(t);
       const long hoff = ((long)b * a.Tq * a.Hq + h) * D;
       uint16_t* qs = q_st + st * C::TILE;
@@ -325,6 +329,24 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   }
 
   // Store: lane = key, register r of block db = head_dim 32*db + 8*(r/4) + 4*hh + r%4.
+  if (a.kv_split > 1) {
+    // Partial sums over this workgroup's query heads (dK unscaled); the
+    // reduction adds the splits in order and rounds.
+    if (key < a.Tkv) {
+      const long part = (long)a.B * a.Tkv * krs;  // elements of one [B, Tkv, Hkv, D] partial
+      float* dkp = a.dkv_part + split * part + kvoff + key * krs;
+      float* dvp = dkp + (long)a.kv_split * part;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * hh;
+          *(f32x4_t*)(dkp + d) = f32x4_t{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
+          *(f32x4_t*)(dvp + d) = f32x4_t{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        }
+    }
+    return;
+  }
   if (key < a.Tkv) {
     uint16_t* dkp = (uint16_t*)a.dk + kvoff + key * krs;
     uint16_t* dvp = (uint16_t*)a.dv + kvoff + key * krs;
@@ -339,6 +361,36 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
                                        pack_bf16(dv[db][4 * g + 2], dv[db][4 * g + 3])};
       }
   }
+}
+
+// Sum of the kv_split partial dK/dV in split order, rounded to bf16 (dK
+// scaled). Each thread handles 8 consecutive elements of [B, Tkv, Hkv, D].
+__global__ __launch_bounds__(256) void attn_dkdv_reduce_kernel(BwdArgs a, long n8) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const long part = n8 * 8;
+  float sk[8] = {}, sv[8] = {};
+  for (int s = 0; s < a.kv_split; ++s) {
+    const f32x4_t* pk = (const f32x4_t*)(a.dkv_part + s * part) + 2 * i;
+    const f32x4_t* pv = (const f32x4_t*)(a.dkv_part + (a.kv_split + s) * part) + 2 * i;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4_t xk = pk[h], xv = pv[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sk[4 * h + e] += xk[e];
+        sv[4 * h + e] += xv[e];
+      }
+    }
+  }
+  u32x4_t wk, wv;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wk[w] = pack_bf16(sk[2 * w] * a.scale, sk[2 * w + 1] * a.scale);
+    wv[w] = pack_bf16(sv[2 * w], sv[2 * w + 1]);
+  }
+  *((u32x4_t*)a.dk + i) = wk;
+  *((u32x4_t*)a.dv + i) = wv;
 }
 
 // --------------------------------------------------------------------- dQ
@@ -555,9 +607,14 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
   if (pass == kBwdPre) {
     launch_delta_any(a, D, true, s);
   } else if (pass == kBwdDkdv) {
-    const long kblocks = (long)a.num_ktiles * a.Hkv * a.B;
-    if (kblocks > 0)
+    const long kblocks = (long)a.kv_split * a.num_ktiles * a.Hkv * a.B;
+    if (kblocks > 0) {
       hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(DkvCfg<D>::THREADS), 0, s, a);
+      if (a.kv_split > 1) {
+        const long n8 = (long)a.B * a.Tkv * a.Hkv * D / 8;
+        hipLaunchKernelGGL(attn_dkdv_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a, n8);
+      }
+    }
   } else {
     const long nqt = (a.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
     const long qblocks = nqt * a.Hq * a.B;

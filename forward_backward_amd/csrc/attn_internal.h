@@ -44,6 +44,9 @@ struct BwdArgs {
   int causal;
   int num_qtiles;          // query tiles of the dQ kernel
   int num_ktiles;          // KV tiles of the dK/dV kernel
+  int kv_split;            // dK/dV workgroups per KV tile, each over heads_per_split query heads of the group
+  int heads_per_split;
+  float* dkv_part;         // workspace when kv_split > 1: fp32 partial dK then dV, [kv_split][B, Tkv, Hkv, D] each
 };
 
 // Arguments of the split-KV decode kernels.
@@ -77,6 +80,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s);
 constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
 constexpr int kBwdBlockM = 64;    // query rows per dQ workgroup
 constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
+constexpr int kBwdFillTarget = 256;  // dK/dV workgroups below which a group's query heads are split (one per CU)
 constexpr int kDecodeTileN = 64;  // keys per decode iteration
 constexpr int kDecodeRows = 64;   // packed query rows per decode workgroup
 constexpr int kDecodeSlots = 256; // decode workgroups resident at once (one per compute unit)

@@ -12,7 +12,9 @@ values: the GPU gets the bf16 bits, the oracle widens them exactly.
 
 The workload shapes follow the probjax attention grids (batch 4, 8 heads,
 head_dim 64/128, lengths 512..8192 and the non-tile-multiple 600/1500/3000),
-the KV-length-masked case and the split-KV decode case.
+the KV-length-masked case, the split-KV decode case, and the pages' GQA suite
+(32 query heads, head_dim 128, batch 1, Lq = Lkv = T) and decode suite (32
+query heads, head_dim 128, 8 or 32 KV heads, batch up to 8, up to 64k keys).
 """
 
 from __future__ import annotations
@@ -137,7 +139,17 @@ def workload_cases(workload_id: int) -> list:
     if workload_id == 4:   # split-KV GQA decode
         return [Case("bf16_gqa_decode_q16_kv16384", 4, 16, 16384, 32, 8, 128, "bf16", False,
                      kv_len_range=(1024, 16384), workload_id=4, decode=True)]
+    if workload_id == 5:   # GQA suite: 32 query heads over 8 KV heads, batch 1, Lq = Lkv = T
+        return [Case(f"bf16_gqa_suite_T{t}", 1, t, t, 32, 8, 128, "bf16", False, workload_id=5)
+                for t in (1024, 2048, 4096, 8192, 16384)]
+    if workload_id == 6:   # decode suite: one query per sequence over a full cache, 8 or 32 KV heads
+        return [Case(f"bf16_decode_suite_B{b}_kv{n}_hkv{hkv}", b, 1, n, 32, hkv, 128, "bf16", False,
+                     workload_id=6, decode=True)
+                for hkv in (8, 32) for b in (1, 8) for n in (4096, 16384, 65536)]
     raise ValueError(f"no workload {workload_id}")
 
 
-NUM_WORKLOADS = 5
+# Workloads 0-4 are the five configurations the parity tests cover in full
+# (0: fp32 correctness case, 1: bf16 d64 grid, 2: headline, 3: KV-length
+# mask, 4: GQA decode); 5 and 6 are the wider GQA and decode suites.
+NUM_WORKLOADS = 7

@@ -85,7 +85,13 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
 /* Bytes of device workspace attn_bwd needs: per query row (B * Hq * Tq rows)
  * 24 bytes, each region rounded up to 256 bytes: D = rowsum(dO * O) and
  * LSE * log2(e) (fp32 each), and 16 bytes of bf16 terms of -LSE/scale and -D
- * that the dK/dV pass adds to its products. */
+ * that the dK/dV pass adds to its products. With GQA (Hq > Hkv, bf16) and
+ * fewer than 256 dK/dV workgroups (B * Hkv * ceil(Tkv / 128)), the query
+ * heads of a group are split over S workgroups per 128 keys (the smallest S
+ * that reaches 256, at most Hq / Hkv) and the workspace adds two fp32
+ * [S, B, Tkv, Hkv, D] arrays of partial dK and dV, summed in split order by
+ * a reduction pass; S depends only on the shape, so results stay bitwise
+ * reproducible. */
 size_t attn_bwd_workspace_size(const attn_params_t* p);
 
 /* Backward: deterministic two-pass scheme without atomics. A pre-kernel

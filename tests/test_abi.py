@@ -85,8 +85,15 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.attn_fwd(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None) == attn.ATTN_ERR_INVALID
     args = [FAKE] * 9
     need = L.attn_bwd_workspace_size(ctypes.byref(p))
-    # D and LSE * log2(e) (fp32 each) and 16 bytes of bf16 row terms per query row
-    assert need == 6 * (2 * 8 * 128 * 4)
+    # D and LSE * log2(e) (fp32 each) and 16 bytes of bf16 row terms per query row ...
+    stat = 2 * 8 * 128 * 4
+    # ... plus, since 2 batches x 2 KV heads x one 128-key tile leave the chip
+    # idle, the 4 query heads of a group split over 4 workgroups whose fp32
+    # partial dK and dV ([4][B, Tkv, Hkv, D] each) are summed afterwards.
+    assert need == 6 * stat + 2 * 4 * (2 * 128 * 2 * 128) * 4
+    assert L.attn_bwd_workspace_size(ctypes.byref(P(Hkv=8))) == 6 * stat  # no group: no split
+    big = P(B=4, Tq=8192, Tkv=8192, Hq=32, Hkv=8)  # 4 * 8 * 64 = 2048 workgroups: no split
+    assert L.attn_bwd_workspace_size(ctypes.byref(big)) == 6 * (4 * 32 * 8192 * 4)
     assert L.attn_bwd(ctypes.byref(p), *args, None, 0, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), *args, FAKE, need - 1, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), None, *args[1:], FAKE, need, None) == attn.ATTN_ERR_INVALID
