@@ -12,8 +12,9 @@ the exact input values the GPU receives (bf16 or fp32, widened exactly).
 Pins (see ``tests/test_oracle.py``): central finite differences, torch float64
 CPU ``scaled_dot_product_attention`` with autograd, a pure-Python brute force,
 closed forms (constant V, single valid key, zero scale, causal row 0, empty
-rows), GQA against repeated K/V, and key-deletion invariance under the KV
-length mask.  Nothing in this package is "parity unpinned".
+rows, the zero-width local window), GQA against repeated K/V, key-deletion
+invariance under the KV length mask, and local windows against torch's band
+helpers and a brute force.  Nothing in this package is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401

@@ -10,8 +10,11 @@ section "Grouped-query attention and decoding"); a per-batch KV length masks
 keys at or past it, and a query row with no valid key returns zeros
 ("H100 (Hopper)", section "Mosaic GPU"); causal masking is the equal-length
 form, key j visible to query i iff j <= i ("Attention performance", section
-"When to use which").  The forward keeps the output and the log-sum-exp
-("Attention performance", section "Memory").
+"When to use which"); a local window, one of the position-only masks the
+fused kernel takes ("Attention performance", section on the default
+attention function), keeps key j for query i iff i - left <= j <= i + right,
+a negative bound meaning no bound on that side.  The forward keeps the output
+and the log-sum-exp ("Attention performance", section "Memory").
 
 Everything here is the plain definition evaluated per (batch, head) on whole
 score matrices: no tiling, no online softmax, no fusion.  Inputs may be any
@@ -30,12 +33,15 @@ def _clamped_len(kv_lens, b: int, tkv: int) -> int:
     return int(min(max(int(kv_lens[b]), 0), tkv))
 
 
-def valid_mask(tq: int, tkv: int, causal: bool, kv_len: int) -> np.ndarray:
+def valid_mask(tq: int, tkv: int, causal: bool, kv_len: int, window=None) -> np.ndarray:
     """Boolean ``[Tq, Tkv]``: key j is visible to query i.
 
     KV-length mask: j < kv_len ("H100 (Hopper)", section "Mosaic GPU").
     Causal, equal-length form: j <= i ("Attention performance", section
     "When to use which": the fast paths take equal-length causal masking).
+    Local window ``(left, right)``: i - left <= j <= i + right, a negative
+    bound meaning none on that side; equal lengths, like the causal form.
+    The masks combine by AND.
     """
     i = np.arange(tq)[:, None]
     j = np.arange(tkv)[None, :]
@@ -44,6 +50,14 @@ def valid_mask(tq: int, tkv: int, causal: bool, kv_len: int) -> np.ndarray:
         if tq != tkv:
             raise ValueError("causal masking is defined here for equal lengths only")
         valid = valid & (j <= i)
+    if window is not None:
+        left, right = int(window[0]), int(window[1])
+        if tq != tkv:
+            raise ValueError("window masks are defined here for equal lengths only")
+        if left >= 0:
+            valid = valid & (j >= i - left)
+        if right >= 0:
+            valid = valid & (j <= i + right)
     return np.broadcast_to(valid, (tq, tkv))
 
 
@@ -94,17 +108,17 @@ def _check_shapes(q, k, v):
     return b, tq, tkv, hq, hkv, d
 
 
-def attention_probs(q, k, scale, causal=False, kv_lens=None, b=0, h=0):
+def attention_probs(q, k, scale, causal=False, kv_lens=None, b=0, h=0, window=None):
     """P ``[Tq, Tkv]`` and LSE ``[Tq]`` of query head ``h`` of batch ``b``."""
     q = _as64(q)
     k = _as64(k)
     _, tq, tkv, hq, hkv, _ = _check_shapes(q, k, k)
     kh = h // (hq // hkv)
-    valid = valid_mask(tq, tkv, causal, _clamped_len(kv_lens, b, tkv))
+    valid = valid_mask(tq, tkv, causal, _clamped_len(kv_lens, b, tkv), window)
     return _head_probs(q[b, :, h, :], k[b, :, kh, :], float(scale), valid)
 
 
-def attention_fwd(q, k, v, scale, causal=False, kv_lens=None, heads=None):
+def attention_fwd(q, k, v, scale, causal=False, kv_lens=None, heads=None, window=None):
     """O = softmax(scale * Q K^T + mask) V and its LSE.
 
     Returns ``o`` float64 ``[B, Tq, Hq, D]`` and ``lse`` float64 ``[B, Hq, Tq]``
@@ -119,14 +133,14 @@ def attention_fwd(q, k, v, scale, causal=False, kv_lens=None, heads=None):
     todo = [(b, h) for b in range(bsz) for h in range(hq)] if heads is None else list(heads)
     for b, h in todo:
         kh = h // g
-        valid = valid_mask(tq, tkv, causal, _clamped_len(kv_lens, b, tkv))
+        valid = valid_mask(tq, tkv, causal, _clamped_len(kv_lens, b, tkv), window)
         p, lse_bh = _head_probs(q[b, :, h, :], k[b, :, kh, :], float(scale), valid)
         o[b, :, h, :] = p @ v[b, :, kh, :]
         lse[b, h, :] = lse_bh
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale, causal=False, kv_lens=None, kv_heads=None):
+def attention_bwd(q, k, v, do, scale, causal=False, kv_lens=None, kv_heads=None, window=None):
     """Gradients of L = sum(dO * O) with respect to Q, K and V.
 
     For each (b, h) with KV head kh = h // G:
@@ -147,7 +161,7 @@ def attention_bwd(q, k, v, do, scale, causal=False, kv_lens=None, kv_heads=None)
     dv = np.full(v.shape, np.nan)
     todo = [(b, kh) for b in range(bsz) for kh in range(hkv)] if kv_heads is None else list(kv_heads)
     for b, kh in todo:
-        valid = valid_mask(tq, tkv, causal, _clamped_len(kv_lens, b, tkv))
+        valid = valid_mask(tq, tkv, causal, _clamped_len(kv_lens, b, tkv), window)
         k_bh = k[b, :, kh, :]
         v_bh = v[b, :, kh, :]
         dk_acc = np.zeros((tkv, d))

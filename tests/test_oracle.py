@@ -273,6 +273,119 @@ def test_partial_head_selection():
     assert np.isnan(dqs[1]).all() and np.isnan(dvs[0, :, 0]).all()
 
 
+# ---------------------------------------------------------------- local window masks
+
+WINDOW_FD_CASES = [
+    # b, tq=tkv, hq, hkv, d, causal, kv_lens, (left, right)
+    (1, 6, 2, 2, 3, False, None, (2, 1)),
+    (2, 6, 4, 2, 3, True, [4, 6], (1, -1)),
+    (1, 7, 3, 1, 2, False, [5], (-1, 0)),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_FD_CASES)
+def test_window_backward_matches_finite_differences(case):
+    b, t, hq, hkv, d, causal, kv_lens, window = case
+    q, k, v, do = make(b, t, t, hq, hkv, d, seed=17)
+    scale = 0.6
+    dq, dk, dv = attention_bwd(q, k, v, do, scale, causal, kv_lens, window=window)
+
+    def loss():
+        o, _ = attention_fwd(q, k, v, scale, causal, kv_lens, window=window)
+        return float(np.sum(do * o))
+
+    for name, x, an in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            orig = x[idx]
+            x[idx] = orig + 1e-6
+            lp = loss()
+            x[idx] = orig - 1e-6
+            lm = loss()
+            x[idx] = orig
+            num[idx] = (lp - lm) / 2e-6
+        assert rel(an, num) < 1e-6, (name, rel(an, num))
+
+
+@pytest.mark.parametrize("window,causal,kv_lens", [((3, 2), False, None), ((5, 0), True, [17, 9]),
+                                                   ((0, 4), False, [12, 20]), ((2, -1), False, None)])
+def test_window_matches_torch_sdpa_float64(window, causal, kv_lens):
+    b, t, hq, hkv, d = 2, 20, 4, 2, 8
+    q, k, v, do = make(b, t, t, hq, hkv, d, seed=23)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attention_fwd(q, k, v, scale, causal, kv_lens, window=window)
+    dq, dk, dv = attention_bwd(q, k, v, do, scale, causal, kv_lens, window=window)
+    left, right = window
+    # The band built with torch's own triangular helpers: tril keeps j <= i + right,
+    # triu keeps j >= i - left.
+    band = torch.ones(t, t, dtype=torch.bool)
+    if right >= 0:
+        band = band.tril(right)
+    if left >= 0:
+        band = band.triu(-left)
+    if causal:
+        band = band & torch.ones(t, t, dtype=torch.bool).tril()
+    mask = band.expand(b, 1, t, t).clone()
+    if kv_lens is not None:
+        for bi, n in enumerate(kv_lens):
+            mask[bi, :, :, n:] = False
+    tq_ = torch.tensor(q.transpose(0, 2, 1, 3), requires_grad=True)
+    tk_ = torch.tensor(k.transpose(0, 2, 1, 3), requires_grad=True)
+    tv_ = torch.tensor(v.transpose(0, 2, 1, 3), requires_grad=True)
+    to = torch.nn.functional.scaled_dot_product_attention(tq_, tk_, tv_, attn_mask=mask, scale=scale,
+                                                          enable_gqa=True)
+    to.backward(torch.tensor(do.transpose(0, 2, 1, 3)))
+    t_ = lambda x: x.detach().numpy().transpose(0, 2, 1, 3)  # noqa: E731
+    assert rel(o, t_(to)) < 1e-12
+    assert rel(dq, t_(tq_.grad)) < 1e-12
+    assert rel(dk, t_(tk_.grad)) < 1e-12
+    assert rel(dv, t_(tv_.grad)) < 1e-12
+
+
+def _brute_window(q, k, v, scale, left, right):
+    out = []
+    for i in range(len(q)):
+        js = [j for j in range(len(k)) if (left < 0 or j >= i - left) and (right < 0 or j <= i + right)]
+        sc = [scale * sum(a * b for a, b in zip(q[i], k[j])) for j in js]
+        z = sum(math.exp(x) for x in sc)
+        out.append([sum(math.exp(x) / z * v[j][c] for j, x in zip(js, sc)) for c in range(len(v[0]))])
+    return out
+
+
+@pytest.mark.parametrize("window", [(1, 1), (0, 2), (3, 0), (-1, 1)])
+def test_window_forward_matches_brute_force(window):
+    q, k, v, _ = make(1, 6, 6, 1, 1, 3, seed=29)
+    o, _ = attention_fwd(q, k, v, 0.8, window=window)
+    bo = _brute_window(q[0, :, 0].tolist(), k[0, :, 0].tolist(), v[0, :, 0].tolist(), 0.8, *window)
+    assert np.allclose(o[0, :, 0], np.array(bo), rtol=0, atol=1e-13)
+
+
+def test_window_closed_forms():
+    b, t, h, d = 2, 9, 3, 4
+    q, k, v, do = make(b, t, t, h, h, d, seed=31)
+    scale = 0.4
+    # A zero-width window: query i sees only key i, so O_i = V_i, LSE_i = S_ii,
+    # dP - D vanishes (one key), dQ = dK = 0 and dV_i = dO_i.
+    o, lse = attention_fwd(q, k, v, scale, window=(0, 0))
+    assert np.allclose(o, v, rtol=0, atol=1e-14)
+    s_diag = scale * np.einsum("bthd,bthd->bht", q, k)
+    assert np.allclose(lse, s_diag, rtol=0, atol=1e-13)
+    dq, dk, dv = attention_bwd(q, k, v, do, scale, window=(0, 0))
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    assert np.allclose(dv, do, rtol=0, atol=1e-14)
+    # Windows that reach past every key are no mask; a left bound of at least
+    # T with right bound 0 is the causal mask.
+    plain = attention_fwd(q, k, v, scale)
+    for w in ((t, t), (-1, -1), (t + 5, -1)):
+        ow, lw = attention_fwd(q, k, v, scale, window=w)
+        assert np.array_equal(ow, plain[0]) and np.array_equal(lw, plain[1])
+    causal = attention_fwd(q, k, v, scale, causal=True)
+    ow, lw = attention_fwd(q, k, v, scale, window=(t, 0))
+    assert np.array_equal(ow, causal[0]) and np.array_equal(lw, causal[1])
+
+
 # ---------------------------------------------------------------- planted mistakes are caught
 
 def _pins_pass():
@@ -284,6 +397,8 @@ def _pins_pass():
         test_gqa_equals_mha_on_repeated_kv()
         test_single_valid_key()
         test_forward_matches_brute_force(True, 3)
+        test_window_matches_torch_sdpa_float64((3, 2), False, None)
+        test_window_closed_forms()
     except AssertionError:
         return False
     return True
@@ -306,14 +421,24 @@ def test_pins_catch_planted_mistakes(monkeypatch):
             return p, np.log(np.maximum(e.sum(axis=1), 1e-300)) + s.max(axis=1)
         return good_probs(q_bh, k_bh, scale, valid)
 
-    def causal_off_by_one(tq, tkv, causal, kv_len):
-        m = good_mask(tq, tkv, False, kv_len).copy()
+    def causal_off_by_one(tq, tkv, causal, kv_len, window=None):
+        m = good_mask(tq, tkv, False, kv_len, window).copy()
         if causal:
             m &= np.arange(tkv)[None, :] < np.arange(tq)[:, None] + 2
         return m
 
+    def window_off_by_one(tq, tkv, causal, kv_len, window=None):
+        m = good_mask(tq, tkv, causal, kv_len).copy()
+        if window is not None:
+            i, j = np.arange(tq)[:, None], np.arange(tkv)[None, :]
+            if window[0] >= 0:
+                m &= j > i - window[0]                   # drops key i - left
+            if window[1] >= 0:
+                m &= j <= i + window[1]
+        return m
+
     for name, fn in (("_head_probs", lse_off), ("_head_probs", transposed_scores),
-                     ("valid_mask", causal_off_by_one)):
+                     ("valid_mask", causal_off_by_one), ("valid_mask", window_off_by_one)):
         monkeypatch.setattr(A, name, fn)
         assert not _pins_pass(), f"planted mistake in {name} ({fn.__name__}) went unnoticed"
         monkeypatch.undo()
