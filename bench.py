@@ -291,7 +291,7 @@ def time_train_steps(case, steps, warmup):
     lse = torch.empty((case.B, case.Hq, case.Tq), dtype=torch.float32, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = attn.bwd_workspace(q, k, case.causal, kv)
-    kw = dict(scale=case.scale, causal=case.causal, kv_lens=kv)
+    kw = dict(scale=case.scale, causal=case.causal, kv_lens=kv, window=case.window)
 
     def step(ev=None):
         attn.fwd(q, k, v, out=o, lse=lse, **kw)
@@ -553,7 +553,7 @@ def main():
     import torch
     from forward_backward_amd import attn
     from forward_backward_amd.inputs import workload_cases
-    from forward_backward_amd.metrics import PEAK_HBM_GBS, PEAK_TFLOPS, attention_flops, decode_bytes
+    from forward_backward_amd.metrics import PEAK_HBM_GBS, PEAK_TFLOPS, attention_flops, decode_bytes, visible_pairs
 
     attn.lib()  # fail loudly without the HIP library
     if not torch.cuda.is_available():
@@ -605,6 +605,17 @@ def main():
         extra["causal"] = {"ms_per_step": round(cms, 4), "tflops": round(cfl / (cms * 1e-3) / 1e12, 2),
                            "per_kernel_ms": {k: round(v, 4) for k, v in cper.items()}}
         log(f"  {cms:.3f} ms/step, {extra['causal']['tflops']} TFLOP/s")
+        (win,) = workload_cases(7)
+        log(f"window {win.name}")
+        wms, wper = time_train_steps(win, args.steps, 1)
+        pairs = visible_pairs(win.Tq, win.Tkv, win.causal, win.window)
+        wfl = 3.5 * 4.0 * win.B * win.Hq * win.D * pairs
+        extra["window"] = {"workload": win.name, "ms_per_step": round(wms, 4),
+                           "tflops_visible": round(wfl / (wms * 1e-3) / 1e12, 2),
+                           "visible_pairs_per_head": pairs,
+                           "flop_count": "3.5 * 4 * B * H * D * visible (query, key) pairs",
+                           "per_kernel_ms": {k: round(v, 4) for k, v in wper.items()}}
+        log(f"  {wms:.3f} ms/step, {extra['window']['tflops_visible']} TFLOP/s over visible pairs")
         (dec,) = workload_cases(4)
         graph_ms, cold, warm, lens = time_decode(dec, args.decode_calls)
         nbytes = decode_bytes(dec.B, dec.Tq, dec.Hq, dec.Hkv, dec.D, lens)

@@ -44,6 +44,8 @@ class Params(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("causal", ctypes.c_int32),
         ("kv_lens", ctypes.c_void_p),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 
@@ -89,9 +91,12 @@ def _check(status: int):
         raise AttnError(status, f"{L.attn_status_string(status).decode()}: {L.attn_last_error().decode()}")
 
 
-def make_params(B, Tq, Tkv, Hq, Hkv, D, dtype=ATTN_BF16, scale=None, causal=False, kv_lens_ptr=None) -> Params:
+def make_params(B, Tq, Tkv, Hq, Hkv, D, dtype=ATTN_BF16, scale=None, causal=False, kv_lens_ptr=None,
+                window=None) -> Params:
+    """``window``: ``(left, right)`` local window bounds, negative = none; None = no window."""
+    left, right = (-1, -1) if window is None else (int(window[0]), int(window[1]))
     return Params(B, Tq, Tkv, Hq, Hkv, D, dtype, float(1.0 / math.sqrt(D) if scale is None else scale),
-                  int(bool(causal)), kv_lens_ptr)
+                  int(bool(causal)), kv_lens_ptr, left, right)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -113,7 +118,7 @@ def _tensor4(name, t):
         raise ValueError(f"{name} must be bfloat16 or float32")
 
 
-def _params_for(q, k, scale, causal, kv_lens):
+def _params_for(q, k, scale, causal, kv_lens, window=None):
     _tensor4("q", q)
     _tensor4("k", k)
     if q.dtype != k.dtype:
@@ -124,12 +129,12 @@ def _params_for(q, k, scale, causal, kv_lens):
     B, Tq, Hq, D = q.shape
     _, Tkv, Hkv, _ = k.shape
     return make_params(B, Tq, Tkv, Hq, Hkv, D, _DTYPES[q.dtype], scale, causal,
-                       None if kv_lens is None else kv_lens.data_ptr())
+                       None if kv_lens is None else kv_lens.data_ptr(), window)
 
 
-def fwd(q, k, v, scale=None, causal=False, kv_lens=None, out=None, lse=None):
+def fwd(q, k, v, scale=None, causal=False, kv_lens=None, out=None, lse=None, window=None):
     """O [B,Tq,Hq,D] (dtype of q) and LSE fp32 [B,Hq,Tq] via attn_fwd."""
-    p = _params_for(q, k, scale, causal, kv_lens)
+    p = _params_for(q, k, scale, causal, kv_lens, window)
     _tensor4("v", v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k")
@@ -139,9 +144,9 @@ def fwd(q, k, v, scale=None, causal=False, kv_lens=None, out=None, lse=None):
     return o, lse_t
 
 
-def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_lens=None, workspace=None):
+def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_lens=None, workspace=None, window=None):
     """dQ, dK, dV via attn_bwd (deterministic two-pass backward)."""
-    p = _params_for(q, k, scale, causal, kv_lens)
+    p = _params_for(q, k, scale, causal, kv_lens, window)
     for name, t, ref in (("v", v, k), ("o", o, q), ("do", do, q)):
         _tensor4(name, t)
         if t.shape != ref.shape or t.dtype != ref.dtype:
@@ -156,30 +161,30 @@ def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_lens=None, workspace=N
     return dq, dk, dv
 
 
-def bwd_workspace(q, k, causal=False, kv_lens=None):
+def bwd_workspace(q, k, causal=False, kv_lens=None, window=None):
     """A device workspace large enough for the backward of this problem."""
-    p = _params_for(q, k, None, causal, kv_lens)
+    p = _params_for(q, k, None, causal, kv_lens, window)
     need = lib().attn_bwd_workspace_size(ctypes.byref(p))
     return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
 
 
-def bwd_preprocess(o, lse, do, ws, q, k, scale=None, causal=False, kv_lens=None):
-    """Pass 1 of the backward: D = rowsum(dO * O) and LSE * log2(e) into the workspace."""
-    p = _params_for(q, k, scale, causal, kv_lens)
+def bwd_preprocess(o, lse, do, ws, q, k, scale=None, causal=False, kv_lens=None, window=None):
+    """Pass 1 of the backward: D = rowsum(dO * O), LSE * log2(e) and the row terms into the workspace."""
+    p = _params_for(q, k, scale, causal, kv_lens, window)
     _check(lib().attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(lse), _ptr(do), _ptr(ws), ws.numel(),
                                      _stream()))
 
 
-def bwd_dkdv(q, k, v, lse, do, ws, dk, dv, scale=None, causal=False, kv_lens=None):
+def bwd_dkdv(q, k, v, lse, do, ws, dk, dv, scale=None, causal=False, kv_lens=None, window=None):
     """Pass 2 of the backward: dK and dV (needs the preprocess pass done)."""
-    p = _params_for(q, k, scale, causal, kv_lens)
+    p = _params_for(q, k, scale, causal, kv_lens, window)
     _check(lib().attn_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
                                _ptr(ws), ws.numel(), _stream()))
 
 
-def bwd_dq(q, k, v, lse, do, ws, dq, scale=None, causal=False, kv_lens=None):
+def bwd_dq(q, k, v, lse, do, ws, dq, scale=None, causal=False, kv_lens=None, window=None):
     """Pass 3 of the backward: dQ (needs the preprocess pass done)."""
-    p = _params_for(q, k, scale, causal, kv_lens)
+    p = _params_for(q, k, scale, causal, kv_lens, window)
     _check(lib().attn_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq), _ptr(ws),
                              ws.numel(), _stream()))
 

@@ -69,6 +69,11 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   if (p->causal && p->Tq != p->Tkv)
     return fail(ATTN_ERR_INVALID, "causal masking needs Tq == Tkv (got %d and %d)", p->Tq, p->Tkv);
   if (op == ATTN_OP_DECODE && p->causal) return fail(ATTN_ERR_INVALID, "decode is non-causal");
+  const bool window = (p->window_left >= 0 && p->window_left < p->Tkv) ||
+                      (p->window_right >= 0 && p->window_right < p->Tkv);
+  if (window && p->Tq != p->Tkv)
+    return fail(ATTN_ERR_INVALID, "window masks need Tq == Tkv (got %d and %d)", p->Tq, p->Tkv);
+  if (window && op == ATTN_OP_DECODE) return fail(ATTN_ERR_INVALID, "decode takes no window mask");
   if (p->D != 64 && p->D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", p->D);
   if (op == ATTN_OP_DECODE && p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is bf16 only");
   // Tile copies address a tile's rows with 32-bit byte offsets.
@@ -79,6 +84,10 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   if (qrows >= kMaxGrid || krows >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
   return ok();
 }
+
+// A window bound as the kernels take it: -1 (no bound) for negative values and
+// for bounds that reach past every key.
+static int window_bound(int32_t w, int32_t tkv) { return (w < 0 || w >= tkv) ? -1 : w; }
 
 // fp32 [B, Hq, Tq] row statistics per array.
 static size_t bwd_stat_bytes(const attn_params_t* p) {
@@ -129,6 +138,7 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
+  a.win_left = window_bound(p->window_left, p->Tkv); a.win_right = window_bound(p->window_right, p->Tkv);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->dtype == ATTN_BF16) {
@@ -166,6 +176,7 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
   a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
+  a.win_left = window_bound(p->window_left, p->Tkv); a.win_right = window_bound(p->window_right, p->Tkv);
   a.num_qtiles = (p->Tq + attn::kBwdBlockM - 1) / attn::kBwdBlockM;
   a.num_ktiles = (p->Tkv + attn::kBwdBlockN - 1) / attn::kBwdBlockN;
   return ATTN_OK;

@@ -106,9 +106,15 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
     dv[i] = f32x16_t{};
   }
 
-  const int qt_begin = a.causal ? k0 / C::BM : 0;
-  const int nqt = (a.Tq + C::BM - 1) / C::BM;
-  const int nq = nqt - qt_begin;
+  // Query rows that see some key of [k0, kmax]: key_hi(i) >= k0 from i_lo on,
+  // key_lo(i) <= kmax up to i_hi.
+  const int kmax = min(k0 + C::BN, kvlim) - 1;
+  int i_lo = a.causal ? k0 : 0;
+  if (a.win_right >= 0) i_lo = max(i_lo, k0 - a.win_right);
+  int i_hi = a.Tq - 1;
+  if (a.win_left >= 0) i_hi = min(i_hi, kmax + a.win_left);
+  const int qt_begin = i_lo / C::BM;
+  const int nq = i_hi >= i_lo ? i_hi / C::BM + 1 - qt_begin : 0;
   const int ntiles = nh * nq;  // (query head, query tile) pairs in a fixed order
 
   if (k0 < kvlim && ntiles > 0) {
@@ -123,7 +129,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
     const float c = a.scale_log2;
     const int tr_row = 4 * hh + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int wave_max_key = k0 + 32 * wave + 31;
+    const int wave_min_key = k0 + 32 * wave;
+    const int wave_max_key = wave_min_key + 31;
 
     // Byte offsets of this lane's reads inside a tile (swizzled layout).
     uint32_t row_off[C::KS], tr_off[C::DB][2];
@@ -171,13 +178,14 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
         dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
       }
     };
-    // Whether tile t needs the element-wise mask (key or causal bound inside
-    // the wave's keys, or a ragged last query tile). The pipeline's extra
+    // Whether tile t needs the element-wise mask (a KV length, causal or
+    // window bound inside the wave's keys, or a ragged last query tile). The pipeline's extra
     // tiles (t < 0, t >= ntiles) compute on zeros or are discarded.
     auto mask_tile = [&](int t) {
       if (t < 0 || t >= ntiles) return false;
       const int q0 = tile_q0(t);
-      return (wave_max_key >= kvlim) || (a.causal && q0 < wave_max_key) || (q0 + C::BM > a.Tq);
+      return (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
+             (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
     };
 
     // Pipeline registers: S/dP accumulators and the packed P/dS operands,
@@ -283,7 +291,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ql = q0m + 32 * SB + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = (key < kvlim) & (!a.causal | (key <= ql)) & (ql < a.Tq);
+          const bool ok = (key >= key_lo(ql, a.win_left)) & (key <= key_hi(ql, kvlim, a.causal, a.win_right)) &
+                          (ql < a.Tq);
           pv[r] = ok ? pv[r] : 0.f;
           dsv[r] = ok ? dsv[r] : 0.f;
         }
@@ -437,10 +446,12 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   const uint16_t* kb = (const uint16_t*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const uint16_t* vb = (const uint16_t*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
 
+  // Keys any row of the tile sees: [key_lo(first row), key_hi(last row)].
   const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
-  int kv_end = kvlim;
-  if (a.causal) kv_end = min(kv_end, q0 + C::BM);
-  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+  const int kv_first = key_lo(q0, a.win_left);
+  const int kv_end = key_hi(q0 + C::BM - 1, kvlim, a.causal, a.win_right) + 1;
+  const int j0 = kv_first / C::BN;  // first key tile
+  const int ntiles = kv_end > kv_first ? (kv_end + C::BN - 1) / C::BN - j0 : 0;
 
   const int qrow = q0 + 32 * wave + l32;
   const bool row_ok = qrow < a.Tq;
@@ -462,6 +473,11 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int wave_min_row = q0 + 32 * wave;
+  // Visible keys of this lane's row, and the keys every row of the wave sees.
+  const int row_lo = key_lo(qrow, a.win_left);
+  const int row_hi = key_hi(qrow, kvlim, a.causal, a.win_right);
+  const int wave_all_lo = key_lo(wave_min_row + 31, a.win_left);
+  const int wave_all_hi = key_hi(wave_min_row, kvlim, a.causal, a.win_right);
   int nrm[C::KS], trd[C::DB][2];
 #pragma unroll
   for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
@@ -472,7 +488,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   }
 
   auto issue = [&](int it, uint16_t* ks, uint16_t* vs) {
-    const int k0 = it * C::BN;
+    const int k0 = (j0 + it) * C::BN;
     dma_tile<D, C::BN, C::THREADS, true>(ks, kb, krs, k0, kv_end, tid);
     dma_tile<D, C::BN, C::THREADS, true>(vs, vb, krs, k0, kv_end, tid);
   };
@@ -516,7 +532,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
         float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
         if constexpr (MASK) {
           const int kk = kblk0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = (kk < kvlim) & (!a.causal | (kk <= qrow));
+          const bool ok = (kk >= row_lo) & (kk <= row_hi);
           p = ok ? p : 0.f;
         }
         dsv[x] = p * (dp[r] - dlt);
@@ -538,8 +554,8 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   // block 1 are interleaved with the softmax of block 0, so that the vector
   // work runs while the matrix core is busy.
   auto compute = [&](int it, const uint16_t* kl, const uint16_t* vl, auto&& issue_next) {
-    const int k0 = it * C::BN;
-    const bool mask_tile = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
+    const int k0 = (j0 + it) * C::BN;
+    const bool mask_tile = (k0 < wave_all_lo) || (k0 + C::BN - 1 > wave_all_hi);
     auto body = [&](auto mask_tag) {
       u32x4_t ka[C::KS], va[C::KS];
       f32x16_t s0, dp0, s1, dp1;

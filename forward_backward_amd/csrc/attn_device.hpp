@@ -254,4 +254,17 @@ __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int tkv)
   return n < 0 ? 0 : (n > tkv ? tkv : n);
 }
 
+// The keys query row i sees are key_lo(i) <= j <= key_hi(i): the AND of the
+// KV length (j < kvlim), the causal mask (j <= i) and the local window
+// (i - left <= j <= i + right; -1 = no bound on that side). Both bounds are
+// non-decreasing in i, so a tile of rows [r0, r1] touches keys
+// [key_lo(r0), key_hi(r1)] and every key of [key_lo(r1), key_hi(r0)].
+__device__ __forceinline__ int key_lo(int i, int left) { return left < 0 ? 0 : max(i - left, 0); }
+__device__ __forceinline__ int key_hi(int i, int kvlim, int causal, int right) {
+  int hi = kvlim - 1;
+  if (causal) hi = min(hi, i);
+  if (right >= 0) hi = min(hi, i + right);
+  return hi;
+}
+
 }  // namespace attn

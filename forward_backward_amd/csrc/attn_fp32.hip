@@ -5,8 +5,8 @@
 // cost about three decimal digits, "GPU and CPU performance", section
 // "Methodology"). It is a correctness path for small problems: one wave per
 // row, lanes over head_dim, dot products by wave reductions. It follows the
-// same masking rules and the same two-pass, atomic-free backward as the bf16
-// kernels, so it is deterministic too.
+// same masking rules (KV length, causal, local window) and the same two-pass,
+// atomic-free backward as the bf16 kernels, so it is deterministic too.
 //
 // The pre-kernel D = rowsum(dO * O) serves both dtypes.
 #include "attn_device.hpp"
@@ -36,8 +36,8 @@ __global__ __launch_bounds__(64) void attn_fwd_fp32_kernel(FwdArgs a) {
   const float* kp = (const float*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const float* vp = (const float*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const long krs = (long)a.Hkv * D;
-  int kv_end = clamp_len(a.kv_lens, b, a.Tkv);
-  if (a.causal) kv_end = min(kv_end, i + 1);
+  const int kv_begin = key_lo(i, a.win_left);
+  const int kv_end = key_hi(i, clamp_len(a.kv_lens, b, a.Tkv), a.causal, a.win_right) + 1;
 
   float q[E], acc[E];
 #pragma unroll
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64) void attn_fwd_fp32_kernel(FwdArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   const float c = a.scale_log2;
-  for (int j = 0; j < kv_end; ++j) {
+  for (int j = kv_begin; j < kv_end; ++j) {
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) part += q[e] * kp[j * krs + lane + 64 * e];
@@ -81,8 +81,8 @@ __global__ __launch_bounds__(64) void attn_dq_fp32_kernel(BwdArgs a) {
   const float* kp = (const float*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const float* vp = (const float*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const long krs = (long)a.Hkv * D;
-  int kv_end = clamp_len(a.kv_lens, b, a.Tkv);
-  if (a.causal) kv_end = min(kv_end, i + 1);
+  const int kv_begin = key_lo(i, a.win_left);
+  const int kv_end = key_hi(i, clamp_len(a.kv_lens, b, a.Tkv), a.causal, a.win_right) + 1;
   const long stat = ((long)b * a.Hq + h) * a.Tq + i;
   const float lse2 = a.lse[stat] * 1.4426950408889634f;
   const float dlt = a.delta[stat];
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64) void attn_dq_fp32_kernel(BwdArgs a) {
     g[e] = ((const float*)a.dout)[qoff + lane + 64 * e];
     acc[e] = 0.f;
   }
-  for (int j = 0; j < kv_end; ++j) {
+  for (int j = kv_begin; j < kv_end; ++j) {
     float ps = 0.f, pd = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -142,7 +142,12 @@ __global__ __launch_bounds__(64) void attn_dkdv_fp32_kernel(BwdArgs a) {
       const float* qp = (const float*)a.q + ((long)b * a.Tq * a.Hq + h) * D;
       const float* gp = (const float*)a.dout + ((long)b * a.Tq * a.Hq + h) * D;
       const long stat0 = ((long)b * a.Hq + h) * a.Tq;
-      for (int i = a.causal ? j : 0; i < a.Tq; ++i) {
+      // Rows that see key j: key_hi(i) >= j from i_lo on, key_lo(i) <= j up to i_hi.
+      int i_lo = a.causal ? j : 0;
+      if (a.win_right >= 0) i_lo = max(i_lo, j - a.win_right);
+      int i_hi = a.Tq - 1;
+      if (a.win_left >= 0) i_hi = min(i_hi, j + a.win_left);
+      for (int i = i_lo; i <= i_hi; ++i) {
         float ps = 0.f, pd = 0.f, qv[E], gv[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {

@@ -23,9 +23,10 @@
 // ahead of V: during iteration j the copies of K_{j+2} and V_{j+1} are in
 // flight while K_{j+1} and V_j are read. Tiles use the swizzled unpadded
 // layout of attn_device.hpp (no bank conflicts for row or transpose reads).
-// Keys at or past min(Tkv, kv_len[b]) and, with causal masking, past the
-// query tile are never read; rows of a partially valid tile are masked
-// element-wise (the copies of rows past the end repeat the last valid row).
+// Only the key tiles that some row of the query tile sees are visited (the
+// KV length, causal and local window bounds, see key_lo / key_hi); rows of a
+// partially visible tile are masked element-wise (the copies of rows past the
+// last visible key repeat it).
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
@@ -71,23 +72,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const uint16_t* kb = (const uint16_t*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const uint16_t* vb = (const uint16_t*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
 
+  // Keys any row of the tile sees: [key_lo(first row), key_hi(last row)].
   const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
-  int kv_end = kvlim;
-  if (a.causal) kv_end = min(kv_end, q0 + C::BM);
-  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+  const int kv_first = key_lo(q0, a.win_left);
+  const int kv_end = key_hi(q0 + C::BM - 1, kvlim, a.causal, a.win_right) + 1;
+  const int j0 = kv_first / C::BN;  // first key tile
+  const int ntiles = kv_end > kv_first ? (kv_end + C::BN - 1) / C::BN - j0 : 0;
 
+  // Copies of the tile-loop's tile j (key tile j0 + j).
   const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
   auto issue_k = [&](int j, uint16_t* dst) {
-    if ((j + 1) * C::BN <= kv_end)
-      kvcopy.copy(dst, kb, krs, j * C::BN);
+    const int k0 = (j0 + j) * C::BN;
+    if (k0 + C::BN <= kv_end)
+      kvcopy.copy(dst, kb, krs, k0);
     else
-      dma_tile<D, C::BN, C::THREADS>(dst, kb, krs, j * C::BN, kv_end, tid);
+      dma_tile<D, C::BN, C::THREADS>(dst, kb, krs, k0, kv_end, tid);
   };
   auto issue_v = [&](int j, uint16_t* dst) {
-    if ((j + 1) * C::BN <= kv_end)
-      kvcopy.copy(dst, vb, krs, j * C::BN);
+    const int k0 = (j0 + j) * C::BN;
+    if (k0 + C::BN <= kv_end)
+      kvcopy.copy(dst, vb, krs, k0);
     else
-      dma_tile<D, C::BN, C::THREADS>(dst, vb, krs, j * C::BN, kv_end, tid);
+      dma_tile<D, C::BN, C::THREADS>(dst, vb, krs, k0, kv_end, tid);
   };
   if (ntiles > 0) {
     issue_k(0, k_s0);
@@ -117,6 +123,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   const float c = a.scale_log2;
   const int wave_min_row = q0 + 32 * wave;
+  // Visible keys of this lane's row, and the keys every row of the wave sees.
+  const int row_lo = key_lo(qrow, a.win_left);
+  const int row_hi = key_hi(qrow, kvlim, a.causal, a.win_right);
+  const int wave_all_lo = key_lo(wave_min_row + 31, a.win_left);
+  const int wave_all_hi = key_hi(wave_min_row, kvlim, a.causal, a.win_right);
 
   // Swizzled LDS offsets of this lane's reads (row blocks of 16 keep the swizzle).
   const int tr_row = 4 * hh + ((lane & 15) >> 2);
@@ -146,14 +157,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   // this stays free of branches.
   auto softmax = [&](auto mask_tag, int j, f32x16_t (&s)[2], u32x4_t (&pf)[4], float& alpha) -> bool {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int k0 = j * C::BN;
+    const int k0 = (j0 + j) * C::BN;
     if constexpr (MASK) {
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * x + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = key < kvlim && (!a.causal || key <= qrow);
+          const bool ok = key >= row_lo && key <= row_hi;
           s[x][r] = ok ? s[x][r] : -INFINITY;
         }
     }
@@ -220,8 +231,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   auto step = [&](int j, const uint16_t* kn, uint16_t* kfree, const uint16_t* vc, uint16_t* vfree) {
     if (j + 2 < ntiles) issue_k(j + 2, kfree);
     if (j + 1 < ntiles) issue_v(j + 1, vfree);
-    const int k0 = j * C::BN;
-    const bool need_mask = (k0 + C::BN > kvlim) || (a.causal && k0 + C::BN - 1 > wave_min_row);
+    const int k0 = (j0 + j) * C::BN;
+    const bool need_mask = (k0 < wave_all_lo) || (k0 + C::BN - 1 > wave_all_hi);
     u32x4_t pf[4];
     float alpha;
     bool any;

@@ -19,6 +19,7 @@ struct FwdArgs {
   float scale;             // softmax scale
   float scale_log2;        // scale * log2(e): the kernels work in base 2
   int causal;
+  int win_left, win_right; // local window bounds, -1 = none (see key_lo / key_hi)
   int num_qtiles;
 };
 
@@ -42,6 +43,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int causal;
+  int win_left, win_right; // local window bounds, -1 = none (see key_lo / key_hi)
   int num_qtiles;          // query tiles of the dQ kernel
   int num_ktiles;          // KV tiles of the dK/dV kernel
   int kv_split;            // dK/dV workgroups per KV tile, each over heads_per_split query heads of the group

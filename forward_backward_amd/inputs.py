@@ -63,6 +63,7 @@ class Case:
     kv_len_range: Optional[tuple] = None      # (lo, hi) inclusive: draw lengths uniformly
     workload_id: int = 0                      # index into WORKLOADS, part of the seed
     decode: bool = False                      # few queries over a long KV cache
+    window: Optional[tuple] = None            # local window (left, right), negative = no bound
 
     @property
     def scale(self) -> float:
@@ -146,10 +147,14 @@ def workload_cases(workload_id: int) -> list:
         return [Case(f"bf16_decode_suite_B{b}_kv{n}_hkv{hkv}", b, 1, n, 32, hkv, 128, "bf16", False,
                      workload_id=6, decode=True)
                 for hkv in (8, 32) for b in (1, 8) for n in (4096, 16384, 65536)]
+    if workload_id == 7:   # headline shape with a causal sliding window of 1024 keys
+        return [Case("bf16_d128_T8192_causal_window1024", 4, 8192, 8192, 8, 8, 128, "bf16", True,
+                     window=(1024, 0), workload_id=7)]
     raise ValueError(f"no workload {workload_id}")
 
 
 # Workloads 0-4 are the five configurations the parity tests cover in full
 # (0: fp32 correctness case, 1: bf16 d64 grid, 2: headline, 3: KV-length
-# mask, 4: GQA decode); 5 and 6 are the wider GQA and decode suites.
-NUM_WORKLOADS = 7
+# mask, 4: GQA decode); 5 and 6 are the wider GQA and decode suites, 7 the
+# local-window case.
+NUM_WORKLOADS = 8

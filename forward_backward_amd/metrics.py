@@ -33,6 +33,22 @@ def effective_flops(H, Tq, kv_lens, D, mode="fwd"):
     return {"fwd": f, "fwd_bwd": 3.5 * f, "fwd+bwd": 3.5 * f, "bwd": 2.5 * f}[mode]
 
 
+def visible_pairs(Tq, Tkv, causal=False, window=None, kv_len=None):
+    """Number of (query, key) pairs the masks leave visible (host arithmetic only)."""
+    n = Tkv if kv_len is None else min(max(int(kv_len), 0), Tkv)
+    left, right = (-1, -1) if window is None else window
+    total = 0
+    for i in range(Tq):
+        lo = 0 if left < 0 else max(i - left, 0)
+        hi = n - 1
+        if causal:
+            hi = min(hi, i)
+        if right >= 0:
+            hi = min(hi, i + right)
+        total += max(hi - lo + 1, 0)
+    return total
+
+
 def decode_bytes(B, Tq, Hq, Hkv, D, kv_lens, elem_bytes=2):
     """Algorithmic HBM bytes of one decode call: K and V rows inside each KV length once, Q and O once."""
     kv = sum(int(n) for n in kv_lens) * Hkv * D * elem_bytes * 2

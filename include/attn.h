@@ -13,6 +13,13 @@
  *   - per-batch KV length (the pages' KVLenMask): keys j >= kv_lens[b] are
  *     skipped; a query row with no valid key returns zeros
  *     ("H100 (Hopper)", section "Mosaic GPU");
+ *   - local window (one of the position-only masks the pages' fused kernel
+ *     takes, "Attention performance", section on the default attention
+ *     function): key j is visible to query i iff
+ *     i - window_left <= j <= i + window_right; a negative bound (or one of
+ *     at least Tkv) means no bound on that side; equal lengths only, like
+ *     the causal form;
+ *   - the masks combine by AND;
  *   - grouped-query attention: query head h reads KV head h / (Hq / Hkv),
  *     without repeating K or V ("Attention performance", section
  *     "Grouped-query attention and decoding").
@@ -50,7 +57,8 @@ typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;
 
 typedef enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID = 1,     /* null pointer, bad sizes, Hq % Hkv != 0, causal with Tq != Tkv, bad scale */
+  ATTN_ERR_INVALID = 1,     /* null pointer, bad sizes, Hq % Hkv != 0, causal or window with Tq != Tkv,
+                               causal or window in decode, bad scale */
   ATTN_ERR_UNSUPPORTED = 2, /* head_dim or dtype this build has no kernel for */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size query */
   ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
@@ -69,6 +77,8 @@ typedef struct {
   float scale;    /* softmax scale, finite and >= 0 (e.g. 1/sqrt(D)) */
   int32_t causal; /* 0 or 1; 1 requires Tq == Tkv */
   const int32_t* kv_lens; /* device int32[B] or NULL (= Tkv for every batch) */
+  int32_t window_left;    /* local window: keys down to i - window_left; < 0 = no bound */
+  int32_t window_right;   /* local window: keys up to i + window_right; < 0 = no bound */
 } attn_params_t;
 
 /* Host-only check of `p` for operation `op` (attn_op_t). Touches no device

@@ -59,6 +59,13 @@ def validate(p, op=attn.OP_FWD):
     ({"dtype": 7}, attn.OP_FWD, attn.ATTN_ERR_INVALID),
     ({"dtype": attn.ATTN_FP32}, attn.OP_DECODE, attn.ATTN_ERR_UNSUPPORTED),
     ({"dtype": attn.ATTN_FP32}, attn.OP_BWD, attn.ATTN_OK),
+    ({"window": (16, 0)}, attn.OP_FWD, attn.ATTN_OK),
+    ({"window": (-1, 3)}, attn.OP_BWD, attn.ATTN_OK),
+    ({"window": (16, 0), "Tq": 64}, attn.OP_FWD, attn.ATTN_ERR_INVALID),      # windows need Tq == Tkv
+    ({"window": (-1, -1), "Tq": 64}, attn.OP_FWD, attn.ATTN_OK),              # no window
+    ({"window": (128, 500), "Tq": 64}, attn.OP_FWD, attn.ATTN_OK),            # reaches past every key
+    ({"window": (8, -1), "Tq": 16, "Tkv": 4096}, attn.OP_DECODE, attn.ATTN_ERR_INVALID),
+    ({"window": (8, 8)}, attn.OP_DECODE, attn.ATTN_ERR_INVALID),
 ])
 def test_validate(kw, op, status):
     assert validate(P(**kw), op) == status

@@ -13,9 +13,10 @@ pytestmark = pytest.mark.gpu
 
 def run_fwd_bwd(case, dev):
     from forward_backward_amd import attn
-    o, lse = attn.fwd(dev["q"], dev["k"], dev["v"], scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"])
+    o, lse = attn.fwd(dev["q"], dev["k"], dev["v"], scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"],
+                      window=case.window)
     dq, dk, dv = attn.bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], scale=case.scale, causal=case.causal,
-                          kv_lens=dev["kv_lens"])
+                          kv_lens=dev["kv_lens"], window=case.window)
     return o, lse, dq, dk, dv
 
 
@@ -26,7 +27,7 @@ def check_bwd(case, kv_heads=None):
     _, _, dq, dk, dv = run_fwd_bwd(case, dev)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle.attention_bwd(f64["q"], f64["k"], f64["v"], f64["do"], case.scale, case.causal,
-                                         f64["kv_lens"], kv_heads=kv_heads)
+                                         f64["kv_lens"], kv_heads=kv_heads, window=case.window)
     gdq, gdk, gdv = to_host64(dq), to_host64(dk), to_host64(dv)
     if kv_heads is not None:
         G = case.Hq // case.Hkv

@@ -28,7 +28,8 @@ SMALL = [
 
 def run_fwd(case, dev):
     from forward_backward_amd import attn
-    return attn.fwd(dev["q"], dev["k"], dev["v"], scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"])
+    return attn.fwd(dev["q"], dev["k"], dev["v"], scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"],
+                    window=case.window)
 
 
 def check_case(case, heads=None):
@@ -37,7 +38,8 @@ def check_case(case, heads=None):
     print(f"[fwd] {case.name}", flush=True)
     o, lse = run_fwd(case, dev)
     torch.cuda.synchronize()
-    ro, rlse = oracle.attention_fwd(f64["q"], f64["k"], f64["v"], case.scale, case.causal, f64["kv_lens"], heads=heads)
+    ro, rlse = oracle.attention_fwd(f64["q"], f64["k"], f64["v"], case.scale, case.causal, f64["kv_lens"], heads=heads,
+                                    window=case.window)
     go, glse = to_host64(o), to_host64(lse)
     if heads is not None:
         sel_o = np.stack([go[b, :, h] for b, h in heads])

@@ -77,3 +77,14 @@ def test_flop_convention_reproduces_pages_records():
             assert abs(ours - float(tflops)) <= 1e-9 * float(tflops), line
             n += 1
     assert n == 317
+
+
+def test_visible_pairs_counts_the_oracle_mask():
+    """The work count the benchmark uses for masked workloads equals the number
+    of True entries of the oracle's mask."""
+    import oracle
+    from forward_backward_amd.metrics import visible_pairs
+    for t, causal, window, kv_len in ((37, False, None, None), (37, True, None, 20), (50, False, (3, 5), None),
+                                      (50, True, (7, -1), 44), (64, False, (-1, 0), None), (9, False, (0, 0), 4)):
+        n = t if kv_len is None else kv_len
+        assert visible_pairs(t, t, causal, window, kv_len) == int(oracle.valid_mask(t, t, causal, n, window).sum())
