@@ -74,7 +74,10 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   if (window && p->Tq != p->Tkv)
     return fail(ATTN_ERR_INVALID, "window masks need Tq == Tkv (got %d and %d)", p->Tq, p->Tkv);
   if (window && op == ATTN_OP_DECODE) return fail(ATTN_ERR_INVALID, "decode takes no window mask");
-  if (p->D != 64 && p->D != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", p->D);
+  if (p->D != 32 && p->D != 64 && p->D != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 32, 64, 128)", p->D);
+  if (p->D == 32 && p->dtype == ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "the fp32 path takes head_dim 64 or 128");
   if (op == ATTN_OP_DECODE && p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is bf16 only");
   // Tile copies address a tile's rows with 32-bit byte offsets.
   if ((long)p->Hq * p->D > (1L << 22) || (long)p->Hkv * p->D > (1L << 22))
@@ -266,9 +269,9 @@ static long decode_segments(const attn_params_t* p) {
 int32_t attn_decode_num_splits(const attn_params_t* p) {
   if (p == nullptr) return 1;
   // One workgroup per compute unit at D = 128 (its LDS ring takes 128 KiB),
-  // two at D = 64; the budget leaves room for the up to one extra range per
+  // two at D = 64 or 32; the budget leaves room for the up to one extra range per
   // segment that rounding adds, so that all ranges run in one wave.
-  const long resident = (long)attn::kDecodeSlots * (p->D == 64 ? 2 : 1);
+  const long resident = (long)attn::kDecodeSlots * (p->D <= 64 ? 2 : 1);
   const long budget = resident - decode_segments(p);
   return budget < 1 ? 1 : (int32_t)budget;
 }

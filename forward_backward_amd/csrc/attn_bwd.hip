@@ -643,8 +643,10 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
 hipError_t launch_bwd_pass_bf16(const BwdArgs& a, int D, int pass, hipStream_t s) {
   if (D == 128)
     launch_pass<128>(a, pass, s);
-  else
+  else if (D == 64)
     launch_pass<64>(a, pass, s);
+  else
+    launch_pass<32>(a, pass, s);
   return hipGetLastError();
 }
 

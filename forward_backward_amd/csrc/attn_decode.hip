@@ -428,8 +428,10 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s) {
   if (D == 128)
     launch_decode<128>(a, s);
-  else
+  else if (D == 64)
     launch_decode<64>(a, s);
+  else
+    launch_decode<32>(a, s);
   return hipGetLastError();
 }
 

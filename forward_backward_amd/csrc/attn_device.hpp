@@ -78,13 +78,18 @@ __device__ __forceinline__ float half_sum(float x) {
 // an unpadded row stride of D elements and store logical 16-byte chunk c of
 // row r at physical chunk c ^ swz_f(r). swz_f takes 16 (D=128) or 8 (D=64,
 // two rows per bank line) distinct values over consecutive rows, and gives
-// the 4 rows of a transpose read disjoint groups of 4 chunks.
+// the 4 rows of a transpose read disjoint groups of 4 chunks. At D=32 four
+// rows share a bank line: rows of equal r % 4 get distinct chunks through
+// (r >> 2) & 3, and a transpose read's 4 consecutive rows never collide.
 template <int D>
 __device__ __forceinline__ int swz_f(int r) {
+  static_assert(D == 32 || D == 64 || D == 128, "head_dim 32, 64 or 128");
   if constexpr (D == 128) {
     return ((r & 3) << 2) | ((r >> 2) & 3);
-  } else {
+  } else if constexpr (D == 64) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  } else {
+    return (r >> 2) & 3;
   }
 }
 

@@ -250,8 +250,10 @@ void launch_delta_any(const BwdArgs& a, int D, bool bf16, hipStream_t s) {
   if ((long)a.B * a.Tq * a.Hq == 0) return;
   if (D == 128)
     launch_delta<128>(a, bf16, s);
-  else
+  else if (D == 64)
     launch_delta<64>(a, bf16, s);
+  else
+    launch_delta<32>(a, bf16, s);
 }
 
 hipError_t launch_fwd_fp32(const FwdArgs& a, int D, hipStream_t s) {

@@ -295,7 +295,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, hipStream_t s) {
   const long blocks = (long)a.num_qtiles * a.Hq * a.B;
   if (blocks == 0) return hipSuccess;
-  if (D == 128) {
+  if (D == 32) {
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else if (D == 128) {
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);

@@ -55,6 +55,9 @@ def validate(p, op=attn.OP_FWD):
     ({"scale": float("nan")}, attn.OP_FWD, attn.ATTN_ERR_INVALID),
     ({"scale": float("inf")}, attn.OP_FWD, attn.ATTN_ERR_INVALID),
     ({"D": 96}, attn.OP_FWD, attn.ATTN_ERR_UNSUPPORTED),
+    ({"D": 32}, attn.OP_FWD, attn.ATTN_OK),
+    ({"D": 32, "Tq": 16, "Tkv": 4096}, attn.OP_DECODE, attn.ATTN_OK),
+    ({"D": 32, "dtype": attn.ATTN_FP32}, attn.OP_BWD, attn.ATTN_ERR_UNSUPPORTED),
     ({"D": 256}, attn.OP_BWD, attn.ATTN_ERR_UNSUPPORTED),
     ({"dtype": 7}, attn.OP_FWD, attn.ATTN_ERR_INVALID),
     ({"dtype": attn.ATTN_FP32}, attn.OP_DECODE, attn.ATTN_ERR_UNSUPPORTED),
