@@ -463,6 +463,26 @@ def gqa_suite(steps):
     return {"shape": "bf16 B1 Hq32 Hkv8 d128 Lq=Lkv=T non-causal, fwd+bwd", "rows": rows}
 
 
+def headdim_sweep(steps):
+    """fwd+bwd at B4 H8 T4096 (non-causal) for head_dim 32, 64 and 128 (bf16)."""
+    from forward_backward_amd.inputs import Case
+    from forward_backward_amd.metrics import attention_flops
+
+    rows = []
+    for d in (32, 64, 128):
+        case = Case(f"bf16_B4_H8_T4096_d{d}", 4, 4096, 4096, 8, 8, d, "bf16", False, workload_id=8)
+        q = device_normal((case.B, case.Tq, case.Hq, d), 1)
+        k = device_normal((case.B, case.Tkv, case.Hkv, d), 2)
+        v = device_normal((case.B, case.Tkv, case.Hkv, d), 3)
+        do = device_normal((case.B, case.Tq, case.Hq, d), 4)
+        ms, _ = _time_steps(q, k, v, do, case, steps, 2)
+        fl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, d, False, "fwd_bwd")
+        rows.append({"D": d, "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)})
+        log(f"  d{d}: {ms:.3f} ms ({rows[-1]['tflops']} TFLOP/s)")
+        del q, k, v, do
+    return {"shape": "bf16 B4 H8 T4096 non-causal, fwd+bwd", "rows": rows}
+
+
 def decode_suite(calls):
     """The pages' decode suite: one query per sequence, 32 query heads, head_dim 128, 8 or 32 KV heads.
 
@@ -635,6 +655,8 @@ def main():
         extra["gqa_suite"] = gqa_suite(max(2, min(args.steps, 5)))
         log("decode suite")
         extra["decode_suite"] = decode_suite(50)
+        log("head_dim sweep")
+        extra["headdim_sweep"] = headdim_sweep(max(2, min(args.steps, 5)))
 
     cpu = None
     if not args.no_cpu_baseline:
