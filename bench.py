@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the causal and decode legs")
     ap.add_argument("--decode-calls", type=int, default=200)
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="also time plain bf16 GEMMs through torch (hipBLASLt) as a practical MFMA ceiling")
     ap.add_argument("--suites", action="store_true",
                     help="also time the GQA suite (fwd+bwd, native GQA against repeated K/V) and the decode suite")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -374,6 +376,29 @@ def time_decode(case, calls, sets=4):
     return replay, cold, warm, [int(x) for x in host["kv_lens"]]
 
 
+def gemm_ceiling():
+    """bf16 GEMM rate of the vendor library through torch: a practical MFMA ceiling for this chip."""
+    import torch
+    rows = []
+    for m, n, k in ((8192, 8192, 8192), (16384, 16384, 8192)):
+        a = device_normal((m, k), 1)
+        b = device_normal((k, n), 2)
+        for _ in range(5):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        rows.append({"m": m, "n": n, "k": k, "ms": round(ms, 4), "tflops": round(2 * m * n * k / (ms * 1e-3) / 1e12, 1)})
+        log(f"  gemm {m}x{n}x{k}: {ms:.3f} ms, {rows[-1]['tflops']} TFLOP/s")
+        del a, b, c
+    return rows
+
+
 def device_normal(shape, seed):
     """Seeded N(0,1) bf16 tensor drawn on the device (timing legs only; no oracle reads it)."""
     import torch
@@ -650,6 +675,9 @@ def main():
         log(f"decode {graph_ms * 1e3:.1f} us/call in a graph ({gbs:.0f} GB/s); eager {cold * 1e3:.1f} us, "
             f"same cache {warm * 1e3:.1f} us")
 
+    if args.gemm_ceiling:
+        log("bf16 GEMM through torch (hipBLASLt)")
+        extra["gemm_ceiling"] = gemm_ceiling()
     if args.suites:
         log("GQA suite")
         extra["gqa_suite"] = gqa_suite(max(2, min(args.steps, 5)))
