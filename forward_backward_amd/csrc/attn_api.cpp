@@ -74,9 +74,9 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   if (window && p->Tq != p->Tkv)
     return fail(ATTN_ERR_INVALID, "window masks need Tq == Tkv (got %d and %d)", p->Tq, p->Tkv);
   if (window && op == ATTN_OP_DECODE) return fail(ATTN_ERR_INVALID, "decode takes no window mask");
-  if (p->D != 32 && p->D != 64 && p->D != 128)
-    return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 32, 64, 128)", p->D);
-  if (p->D == 32 && p->dtype == ATTN_FP32)
+  if (p->D != 32 && p->D != 64 && p->D != 128 && p->D != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 32, 64, 128, 256)", p->D);
+  if ((p->D == 32 || p->D == 256) && p->dtype == ATTN_FP32)
     return fail(ATTN_ERR_UNSUPPORTED, "the fp32 path takes head_dim 64 or 128");
   if (op == ATTN_OP_DECODE && p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is bf16 only");
   // Tile copies address a tile's rows with 32-bit byte offsets.

@@ -372,6 +372,227 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   }
 }
 
+// dK/dV at head_dim 256. The accumulators of all 256 columns would take 256
+// registers per lane besides K and V (128), so each workgroup forms one
+// 128-column half of dK and dV (S and dP are recomputed per half), and a
+// 64-row tile of Q and dO (32 KiB each) would overfill the LDS with three
+// stages; this variant walks 32-row tiles through a two-stage ring without
+// the cross-block pipeline: per tile S, dP (with the row terms), the masked
+// softmax, then the dV/dK products of the half.
+struct DkvWideCfg {
+  static constexpr int D = 256;
+  static constexpr int HALF = 128;          // dK/dV columns per workgroup
+  static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave
+  static constexpr int BM = 32;             // query rows per tile
+  static constexpr int THREADS = 256;
+  static constexpr int KS = D / 16;
+  static constexpr int DBH = HALF / 32;
+  static constexpr int TILE = BM * D;
+};
+
+__global__ __launch_bounds__(256) void attn_dkdv_d256_kernel(BwdArgs a) {
+  using C = DkvWideCfg;
+  constexpr int D = C::D;
+  constexpr int TB = C::TILE * 2;
+  constexpr int R_OFF = 0;                  // row terms: 16 bytes per query row, two stages
+  constexpr int Q_OFF = 2 * C::BM * 16;
+  constexpr int G_OFF = Q_OFF + 2 * TB;
+  __shared__ __attribute__((aligned(16))) char smem[G_OFF + 2 * TB];
+  uint16_t* const q_st = (uint16_t*)(smem + Q_OFF);
+  uint16_t* const g_st = (uint16_t*)(smem + G_OFF);
+  uint16_t* const r_st = (uint16_t*)(smem + R_OFF);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = bid % a.num_ktiles;
+  int rest = bid / a.num_ktiles;
+  const int ch = rest % 2;                   // column half of dK/dV
+  rest /= 2;
+  const int kh = rest % a.Hkv;
+  rest /= a.Hkv;
+  const int b = rest % a.B;
+  const int split = rest / a.B;
+  const int G = a.Hq / a.Hkv;
+  const int h_lo = split * a.heads_per_split;
+  const int nh = min(a.heads_per_split, G - h_lo);
+  const int k0 = kt * C::BN;
+  const int key = k0 + 32 * wave + l32;
+
+  const long krs = (long)a.Hkv * D;
+  const long qrs = (long)a.Hq * D;
+  const long kvoff = ((long)b * a.Tkv * a.Hkv + kh) * D;
+  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
+
+  f32x16_t dk[C::DBH], dv[C::DBH];
+#pragma unroll
+  for (int i = 0; i < C::DBH; ++i) {
+    dk[i] = f32x16_t{};
+    dv[i] = f32x16_t{};
+  }
+
+  const int kmax = min(k0 + C::BN, kvlim) - 1;
+  int i_lo = a.causal ? k0 : 0;
+  if (a.win_right >= 0) i_lo = max(i_lo, k0 - a.win_right);
+  int i_hi = a.Tq - 1;
+  if (a.win_left >= 0) i_hi = min(i_hi, kmax + a.win_left);
+  const int qt_begin = i_lo / C::BM;
+  const int nq = i_hi >= i_lo ? i_hi / C::BM + 1 - qt_begin : 0;
+  const int ntiles = nh * nq;
+
+  if (k0 < kvlim && ntiles > 0) {
+    u32x4_t kf[C::KS], vf[C::KS];
+    const bool key_ok = key < kvlim;
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) {
+      kf[t] = key_ok ? gload16((const uint16_t*)a.k + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+      vf[t] = key_ok ? gload16((const uint16_t*)a.v + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    }
+    const float c = a.scale_log2;
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int wave_min_key = k0 + 32 * wave;
+    const int wave_max_key = wave_min_key + 31;
+    int nrm[C::KS], trd[C::DBH][2];
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
+#pragma unroll
+    for (int db = 0; db < C::DBH; ++db) {
+      trd[db][0] = swz_off<D>(tr_row, C::HALF * ch + 32 * db + tr_col);
+      trd[db][1] = swz_off<D>(tr_row + 8, C::HALF * ch + 32 * db + tr_col);
+    }
+    const unsigned one2 = 0x3F803F80u, one1 = 0x00003F80u;
+    const u32x4_t sel_s = hh == 0 ? u32x4_t{one2, one1, 0, 0} : u32x4_t{0, 0, 0, 0};
+    const u32x4_t sel_d = hh == 0 ? u32x4_t{0, 0, one2, one1} : u32x4_t{0, 0, 0, 0};
+
+    auto tile_q0 = [&](int t) { return (qt_begin + t % nq) * C::BM; };
+    auto issue = [&](int t, int st) {
+      const int h = kh * G + h_lo + t / nq;
+      const int q0 = tile_q0(t);
+      const long hoff = ((long)b * a.Tq * a.Hq + h) * D;
+      dma_tile<D, C::BM, C::THREADS>(q_st + st * C::TILE, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
+      dma_tile<D, C::BM, C::THREADS>(g_st + st * C::TILE, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
+      if (wave == 0 && lane < C::BM) {
+        int i = q0 + lane;
+        i = i < a.Tq ? i : a.Tq - 1;
+        dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
+      }
+    };
+
+    auto tile = [&](int t, int st) {
+      const int q0 = tile_q0(t);
+      const bool mask = (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
+                        (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
+      const uint16_t* qs = q_st + st * C::TILE;
+      const uint16_t* gs = g_st + st * C::TILE;
+      // S and dP with the row terms (-LSE/scale, -D) through one extra k-step.
+      u32x4_t qa[2], ga[2];
+      qa[0] = lds_read16(qs + nrm[0]);
+      ga[0] = lds_read16(gs + nrm[0]);
+      qa[1] = lds_read16(qs + nrm[1]);
+      ga[1] = lds_read16(gs + nrm[1]);
+      f32x16_t sv = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int m = 0; m < C::KS; ++m) {
+        sv = mfma_bf16(qa[m & 1], kf[m], sv);
+        dp = mfma_bf16(ga[m & 1], vf[m], dp);
+        if (m + 2 < C::KS) {
+          qa[m & 1] = lds_read16(qs + nrm[m + 2]);
+          ga[m & 1] = lds_read16(gs + nrm[m + 2]);
+        }
+      }
+      const u32x4_t terms = lds_read16(r_st + (st * C::BM + l32) * 8);
+      sv = mfma_bf16(terms, sel_s, sv);
+      dp = mfma_bf16(terms, sel_d, dp);
+      u32x4_t pk_p[2], pk_d[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int r = 8 * u + x;
+          const float p = fast_exp2(sv[r] * c);
+          pv[x] = p;
+          dsv[x] = p * dp[r];
+        }
+        if (mask) {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int r = 8 * u + x;
+            const int ql = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = (key >= key_lo(ql, a.win_left)) &
+                            (key <= key_hi(ql, kvlim, a.causal, a.win_right)) & (ql < a.Tq);
+            pv[x] = ok ? pv[x] : 0.f;
+            dsv[x] = ok ? dsv[x] : 0.f;
+          }
+        }
+        pk_p[u] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                          pack_bf16(pv[6], pv[7])};
+        pk_d[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                          pack_bf16(dsv[6], dsv[7])};
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS over this half's columns.
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < C::DBH; ++db) {
+          const u32x2_t g0 = lds_read_tr(gs + 16 * u * D + trd[db][0]);
+          const u32x2_t g1 = lds_read_tr(gs + 16 * u * D + trd[db][1]);
+          const u32x2_t x0 = lds_read_tr(qs + 16 * u * D + trd[db][0]);
+          const u32x2_t x1 = lds_read_tr(qs + 16 * u * D + trd[db][1]);
+          dv[db] = mfma_bf16(u32x4_t{g0[0], g0[1], g1[0], g1[1]}, pk_p[u], dv[db]);
+          dk[db] = mfma_bf16(u32x4_t{x0[0], x0[1], x1[0], x1[1]}, pk_d[u], dk[db]);
+        }
+    };
+
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int st = t & 1;
+      if (t + 1 < ntiles) issue(t + 1, st ^ 1);
+      tile(t, st);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // Store this half's columns: lane = key, register r of block db = column
+  // HALF*ch + 32*db + 8*(r/4) + 4*hh + r%4.
+  if (key < a.Tkv) {
+    if (a.kv_split > 1) {
+      const long part = (long)a.B * a.Tkv * krs;
+      float* dkp = a.dkv_part + split * part + kvoff + key * krs + C::HALF * ch;
+      float* dvp = dkp + (long)a.kv_split * part;
+#pragma unroll
+      for (int db = 0; db < C::DBH; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * hh;
+          *(f32x4_t*)(dkp + d) = f32x4_t{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
+          *(f32x4_t*)(dvp + d) = f32x4_t{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        }
+    } else {
+      uint16_t* dkp = (uint16_t*)a.dk + kvoff + key * krs + C::HALF * ch;
+      uint16_t* dvp = (uint16_t*)a.dv + kvoff + key * krs + C::HALF * ch;
+#pragma unroll
+      for (int db = 0; db < C::DBH; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * hh;
+          *(u32x2_t*)(dkp + d) = u32x2_t{pack_bf16(dk[db][4 * g] * a.scale, dk[db][4 * g + 1] * a.scale),
+                                         pack_bf16(dk[db][4 * g + 2] * a.scale, dk[db][4 * g + 3] * a.scale)};
+          *(u32x2_t*)(dvp + d) = u32x2_t{pack_bf16(dv[db][4 * g], dv[db][4 * g + 1]),
+                                         pack_bf16(dv[db][4 * g + 2], dv[db][4 * g + 3])};
+        }
+    }
+  }
+}
+
 // Sum of the kv_split partial dK/dV in split order, rounded to bf16 (dK
 // scaled). Each thread handles 8 consecutive elements of [B, Tkv, Hkv, D].
 __global__ __launch_bounds__(256) void attn_dkdv_reduce_kernel(BwdArgs a, long n8) {
@@ -582,10 +803,57 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
       softmax(mask_tag, k0 + 32, s1, dp1, dsb);
       dq_mfma(kt, dsb);
     };
-    if (mask_tile)
-      body(std::true_type{});
-    else
-      body(std::false_type{});
+    // head_dim 256: a block's K/V fragments alone would take 128 registers,
+    // so they stream through a two-deep ring and the transposed K fragments
+    // are read per 16-key half; one block at a time.
+    auto body_wide = [&](auto mask_tag) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint16_t* krow = kl + 32 * j * D;
+        const uint16_t* vrow = vl + 32 * j * D;
+        u32x4_t ka[2], va[2];
+        ka[0] = lds_read16(krow + nrm[0]);
+        va[0] = lds_read16(vrow + nrm[0]);
+        ka[1] = lds_read16(krow + nrm[1]);
+        va[1] = lds_read16(vrow + nrm[1]);
+        f32x16_t sj = f32x16_t{}, dpj = f32x16_t{};
+#pragma unroll
+        for (int t = 0; t < C::KS; ++t) {
+          sj = mfma_bf16(ka[t & 1], qf[t], sj);
+          dpj = mfma_bf16(va[t & 1], gf[t], dpj);
+          if (t + 2 < C::KS) {
+            ka[t & 1] = lds_read16(krow + nrm[t + 2]);
+            va[t & 1] = lds_read16(vrow + nrm[t + 2]);
+          }
+        }
+        u32x4_t dsb[2];
+        softmax(mask_tag, k0 + 32 * j, sj, dpj, dsb);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x2_t kt[C::DB][2];
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            kt[db][0] = lds_read_tr(krow + 16 * u * D + trd[db][0]);
+            kt[db][1] = lds_read_tr(krow + 16 * u * D + trd[db][1]);
+          }
+          if (j == 0 && u == 0) issue_next();
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+            acc[db] = mfma_bf16(u32x4_t{kt[db][0][0], kt[db][0][1], kt[db][1][0], kt[db][1][1]}, dsb[u], acc[db]);
+        }
+      }
+    };
+    if constexpr (D > 128) {
+      if (mask_tile)
+        body_wide(std::true_type{});
+      else
+        body_wide(std::false_type{});
+    } else {
+      if (mask_tile)
+        body(std::true_type{});
+      else
+        body(std::false_type{});
+    }
   };
 
   auto step = [&](int it, uint16_t* nk, uint16_t* nv, const uint16_t* ck, const uint16_t* cv) {
@@ -625,7 +893,10 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
   } else if (pass == kBwdDkdv) {
     const long kblocks = (long)a.kv_split * a.num_ktiles * a.Hkv * a.B;
     if (kblocks > 0) {
-      hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(DkvCfg<D>::THREADS), 0, s, a);
+      if constexpr (D == 256)
+        hipLaunchKernelGGL(attn_dkdv_d256_kernel, dim3((unsigned)(2 * kblocks)), dim3(DkvWideCfg::THREADS), 0, s, a);
+      else
+        hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(DkvCfg<D>::THREADS), 0, s, a);
       if (a.kv_split > 1) {
         const long n8 = (long)a.B * a.Tkv * a.Hkv * D / 8;
         hipLaunchKernelGGL(attn_dkdv_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a, n8);
@@ -643,6 +914,8 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
 hipError_t launch_bwd_pass_bf16(const BwdArgs& a, int D, int pass, hipStream_t s) {
   if (D == 128)
     launch_pass<128>(a, pass, s);
+  else if (D == 256)
+    launch_pass<256>(a, pass, s);
   else if (D == 64)
     launch_pass<64>(a, pass, s);
   else

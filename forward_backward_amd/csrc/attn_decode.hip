@@ -41,7 +41,7 @@ struct DecCfg {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int TILE = BN * D;         // elements of one K or V tile (swizzled, unpadded)
-  static constexpr int NST = 4;               // LDS ring stages
+  static constexpr int NST = D > 128 ? 2 : 4;  // LDS ring stages (two 64 KiB stages at head_dim 256)
   // Global->LDS copy instructions per wave per stage (K and V): 1 KiB each.
   static constexpr int COPIES = 2 * TILE * 2 / 1024 / (THREADS / 64);
   // LDS for the final merge: per row block, O (16 * DB floats per lane) plus max and sum.
@@ -428,6 +428,8 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s) {
   if (D == 128)
     launch_decode<128>(a, s);
+  else if (D == 256)
+    launch_decode<256>(a, s);
   else if (D == 64)
     launch_decode<64>(a, s);
   else

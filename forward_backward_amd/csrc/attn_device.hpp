@@ -81,10 +81,12 @@ __device__ __forceinline__ float half_sum(float x) {
 // the 4 rows of a transpose read disjoint groups of 4 chunks. At D=32 four
 // rows share a bank line: rows of equal r % 4 get distinct chunks through
 // (r >> 2) & 3, and a transpose read's 4 consecutive rows never collide.
+// At D=256 a row spans two bank lines and the D=128 pattern applies to the
+// low four bits of the chunk index.
 template <int D>
 __device__ __forceinline__ int swz_f(int r) {
-  static_assert(D == 32 || D == 64 || D == 128, "head_dim 32, 64 or 128");
-  if constexpr (D == 128) {
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head_dim 32, 64, 128 or 256");
+  if constexpr (D >= 128) {
     return ((r & 3) << 2) | ((r >> 2) & 3);
   } else if constexpr (D == 64) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
@@ -175,7 +177,15 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long
 
 // Copy with a wave-uniform 64-bit base (scalar registers) and a per-lane
 // 32-bit byte offset: the address arithmetic is one scalar add per tile.
+// The base is made explicitly wave-uniform (both halves through
+// readfirstlane) so that it always lands in scalar registers. readfirstlane
+// returns a signed int: each half is taken back as uint32_t before widening,
+// or a low half with bit 31 set would sign-extend over the high half.
 __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const void* sbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -184,7 +194,7 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(base), "s"(lds)
+      : "v"(voff), "s"(sbase), "s"(lds)
       : "memory");
 }
 

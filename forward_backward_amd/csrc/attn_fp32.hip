@@ -250,6 +250,8 @@ void launch_delta_any(const BwdArgs& a, int D, bool bf16, hipStream_t s) {
   if ((long)a.B * a.Tq * a.Hq == 0) return;
   if (D == 128)
     launch_delta<128>(a, bf16, s);
+  else if (D == 256)
+    launch_delta<256>(a, bf16, s);
   else if (D == 64)
     launch_delta<64>(a, bf16, s);
   else

@@ -47,8 +47,10 @@ struct FwdCfg {
   static constexpr int TILE = BN * D;         // elements of one K or V tile
 };
 
+// Two workgroups per compute unit up to head_dim 128; at 256 the output
+// accumulators alone take 128 registers per lane and the K/V rings 128 KiB.
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_s0[C::TILE], k_s1[C::TILE], v_s0[C::TILE], v_s1[C::TILE];
 
@@ -297,6 +299,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int D, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (D == 32) {
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else if (D == 256) {
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<256>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   } else if (D == 128) {
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   } else {

@@ -169,3 +169,37 @@ def test_empty_problems(name, B, Tq, Tkv, causal, dtype, D):
         assert od.shape == q.shape
         if Tkv == 0:
             assert bool(torch.all(od == 0)) and bool(torch.all(torch.isneginf(lsed)))
+
+
+def test_inputs_at_addresses_with_bit31_of_the_low_word_set():
+    """Tile copies take their base address in scalar registers, split in 32-bit
+    halves; a low half with bit 31 set must not spill into the high half (a
+    sign extension there once made the copies read far outside the tensors).
+    The inputs are placed inside one large buffer at an address whose low
+    32 bits are >= 2^31, then checked against a copy at an ordinary address."""
+    import torch
+    from forward_backward_amd import attn
+    from helpers import device_inputs, rel_err, to_host64
+    case = Case("bit31_d128_T512_gqa", 1, 512, 512, 4, 2, 128, workload_id=130)
+    _, dev, _ = device_inputs(case)
+    big = torch.empty(2**32 + 2**26, dtype=torch.uint8, device="cuda")
+    base = big.data_ptr()
+    off = (2**31 + 4096 - (base & 0xFFFFFFFF)) % 2**32  # low word of base + off is 2^31 + 4096
+    placed = {}
+    for name in ("q", "k", "v", "do"):
+        t = dev[name]
+        nbytes = t.numel() * 2
+        view = big[off:off + nbytes].view(torch.bfloat16).view(t.shape)
+        view.copy_(t)
+        assert (view.data_ptr() & 0xFFFFFFFF) >= 2**31
+        placed[name] = view
+        off += (nbytes + 4095) // 4096 * 4096
+    o_a, lse_a = attn.fwd(placed["q"], placed["k"], placed["v"], scale=case.scale)
+    g_a = attn.bwd(placed["q"], placed["k"], placed["v"], o_a, lse_a, placed["do"], scale=case.scale)
+    o_b, lse_b = attn.fwd(dev["q"], dev["k"], dev["v"], scale=case.scale)
+    g_b = attn.bwd(dev["q"], dev["k"], dev["v"], o_b, lse_b, dev["do"], scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a.view(torch.int16), o_b.view(torch.int16)) and torch.equal(lse_a, lse_b)
+    for a, b in zip(g_a, g_b):
+        assert rel_err(to_host64(a), to_host64(b)) == 0.0
+    del big
