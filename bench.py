@@ -489,12 +489,12 @@ def gqa_suite(steps):
 
 
 def headdim_sweep(steps):
-    """fwd+bwd at B4 H8 T4096 (non-causal) for head_dim 32, 64 and 128 (bf16)."""
+    """fwd+bwd at B4 H8 T4096 (non-causal) for head_dim 32, 64, 128 and 256 (bf16)."""
     from forward_backward_amd.inputs import Case
     from forward_backward_amd.metrics import attention_flops
 
     rows = []
-    for d in (32, 64, 128):
+    for d in (32, 64, 128, 256):
         case = Case(f"bf16_B4_H8_T4096_d{d}", 4, 4096, 4096, 8, 8, d, "bf16", False, workload_id=8)
         q = device_normal((case.B, case.Tq, case.Hq, d), 1)
         k = device_normal((case.B, case.Tkv, case.Hkv, d), 2)
