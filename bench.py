@@ -58,6 +58,7 @@ def parse_args():
     ap.add_argument("--decode-calls", type=int, default=200)
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="also time plain bf16 GEMMs through torch (hipBLASLt) as a practical MFMA ceiling")
+    ap.add_argument("--fp32-suite", action="store_true", help="time the fp32 grid (batch 4, 8 heads, head_dim 64/128)")
     ap.add_argument("--suites", action="store_true",
                     help="also time the GQA suite (fwd+bwd, native GQA against repeated K/V) and the decode suite")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -399,12 +400,12 @@ def gemm_ceiling():
     return rows
 
 
-def device_normal(shape, seed):
-    """Seeded N(0,1) bf16 tensor drawn on the device (timing legs only; no oracle reads it)."""
+def device_normal(shape, seed, dtype="bf16"):
+    """Seeded N(0,1) tensor drawn on the device (timing legs only; no oracle reads it)."""
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
-    return torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
 def _time_steps(q, k, v, do, case, steps, warmup):
@@ -506,6 +507,44 @@ def headdim_sweep(steps):
         log(f"  d{d}: {ms:.3f} ms ({rows[-1]['tflops']} TFLOP/s)")
         del q, k, v, do
     return {"shape": "bf16 B4 H8 T4096 non-causal, fwd+bwd", "rows": rows}
+
+
+FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+
+
+def fp32_suite(steps):
+    """The pages' fp32 grid: batch 4, 8 heads, head_dim 64 and 128, T = 1024 ... 8192, fwd and fwd+bwd."""
+    import torch
+    from forward_backward_amd import attn
+    from forward_backward_amd.inputs import workload_cases
+    from forward_backward_amd.metrics import attention_flops
+
+    rows = []
+    for case in workload_cases(8):
+        q = device_normal((case.B, case.Tq, case.Hq, case.D), 1, "fp32")
+        k = device_normal((case.B, case.Tkv, case.Hkv, case.D), 2, "fp32")
+        v = device_normal((case.B, case.Tkv, case.Hkv, case.D), 3, "fp32")
+        do = device_normal((case.B, case.Tq, case.Hq, case.D), 4, "fp32")
+        ms, _ = _time_steps(q, k, v, do, case, steps, 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            attn.fwd(q, k, v, scale=case.scale, causal=case.causal)
+        e0.record()
+        for _ in range(steps):
+            attn.fwd(q, k, v, scale=case.scale, causal=case.causal)
+        e1.record()
+        torch.cuda.synchronize()
+        fwd_ms = e0.elapsed_time(e1) / steps
+        fl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, case.causal, "fwd_bwd")
+        ffl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, case.causal, "fwd")
+        tf, ftf = fl / (ms * 1e-3) / 1e12, ffl / (fwd_ms * 1e-3) / 1e12
+        rows.append({"case": case.name, "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(ftf, 1),
+                     "fwd_bwd_ms": round(ms, 4), "fwd_bwd_tflops": round(tf, 1),
+                     "fwd_bwd_frac_fp32_peak": round(tf / FP32_PEAK_TFLOPS, 3)})
+        log(f"  {case.name}: fwd {fwd_ms:.3f} ms ({ftf:.1f} TFLOP/s), fwd+bwd {ms:.3f} ms ({tf:.1f} TFLOP/s, "
+            f"{tf / FP32_PEAK_TFLOPS:.0%} of the fp32 matrix peak)")
+        del q, k, v, do
+    return {"shape": "fp32 B4 H8, head_dim 64/128", "peak_tflops": FP32_PEAK_TFLOPS, "rows": rows}
 
 
 def decode_suite(calls):
@@ -685,6 +724,9 @@ def main():
         extra["decode_suite"] = decode_suite(50)
         log("head_dim sweep")
         extra["headdim_sweep"] = headdim_sweep(max(2, min(args.steps, 5)))
+    if args.suites or args.fp32_suite:
+        log("fp32 suite")
+        extra["fp32_suite"] = fp32_suite(max(2, min(args.steps, 5)))
 
     cpu = None
     if not args.no_cpu_baseline:

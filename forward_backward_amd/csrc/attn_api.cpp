@@ -76,8 +76,8 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   if (window && op == ATTN_OP_DECODE) return fail(ATTN_ERR_INVALID, "decode takes no window mask");
   if (p->D != 32 && p->D != 64 && p->D != 128 && p->D != 256)
     return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d (supported: 32, 64, 128, 256)", p->D);
-  if ((p->D == 32 || p->D == 256) && p->dtype == ATTN_FP32)
-    return fail(ATTN_ERR_UNSUPPORTED, "the fp32 path takes head_dim 64 or 128");
+  if (p->D == 256 && p->dtype == ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "the fp32 path takes head_dim 32, 64 or 128");
   if (op == ATTN_OP_DECODE && p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode is bf16 only");
   // Tile copies address a tile's rows with 32-bit byte offsets.
   if ((long)p->Hq * p->D > (1L << 22) || (long)p->Hkv * p->D > (1L << 22))
@@ -144,14 +144,12 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   a.win_left = window_bound(p->window_left, p->Tkv); a.win_right = window_bound(p->window_right, p->Tkv);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (p->dtype == ATTN_BF16) {
-    a.num_qtiles = (p->Tq + attn::kFwdBlockM - 1) / attn::kFwdBlockM;
-    if ((long)a.num_qtiles * a.Hq * a.B >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+  a.num_qtiles = (p->Tq + attn::kFwdBlockM - 1) / attn::kFwdBlockM;
+  if ((long)a.num_qtiles * a.Hq * a.B >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+  if (p->dtype == ATTN_BF16)
     e = attn::launch_fwd_bf16(a, p->D, s);
-  } else {
-    a.num_qtiles = p->Tq;
+  else
     e = attn::launch_fwd_fp32(a, p->D, s);
-  }
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
   return ok();
 }

@@ -150,11 +150,14 @@ def workload_cases(workload_id: int) -> list:
     if workload_id == 7:   # headline shape with a causal sliding window of 1024 keys
         return [Case("bf16_d128_T8192_causal_window1024", 4, 8192, 8192, 8, 8, 128, "bf16", True,
                      window=(1024, 0), workload_id=7)]
+    if workload_id == 8:   # fp32 grid: batch 4, 8 heads, head_dim 64 and 128
+        return [Case(f"fp32_d{d}_T{t}_{'causal' if c else 'full'}", 4, t, t, 8, 8, d, "fp32", c, workload_id=8)
+                for d in (64, 128) for t in (1024, 2048, 4096, 8192) for c in (False, True)]
     raise ValueError(f"no workload {workload_id}")
 
 
 # Workloads 0-4 are the five configurations the parity tests cover in full
 # (0: fp32 correctness case, 1: bf16 d64 grid, 2: headline, 3: KV-length
 # mask, 4: GQA decode); 5 and 6 are the wider GQA and decode suites, 7 the
-# local-window case.
-NUM_WORKLOADS = 8
+# local-window case, 8 the fp32 grid.
+NUM_WORKLOADS = 9

@@ -28,7 +28,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
  *     in [B, T, H, D] order (row stride H*D elements) and 16-byte aligned.
  *     Q, dO, O, dQ: [B, Tq, Hq, D]; K, V, dK, dV: [B, Tkv, Hkv, D].
- *     Tensors are bf16 or fp32 as given by attn_params_t.dtype. A tensor
+ *     Tensors are bf16 or fp32 as given by attn_params_t.dtype (fp32 is
+ *     computed in fp32 throughout, on the fp32 matrix cores). A tensor
  *     with no elements (B, Tq or Tkv = 0) may be passed as NULL; any other
  *     NULL or misaligned tensor pointer -> ATTN_ERR_INVALID.
  *   - LSE is fp32 [B, Hq, Tq], natural logarithm, -inf on rows with no
@@ -59,7 +60,8 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, bad sizes, Hq % Hkv != 0, causal or window with Tq != Tkv,
                                causal or window in decode, bad scale */
-  ATTN_ERR_UNSUPPORTED = 2, /* head_dim or dtype this build has no kernel for */
+  ATTN_ERR_UNSUPPORTED = 2, /* head_dim or dtype this build has no kernel for: D outside {32, 64, 128, 256},
+                               fp32 with D = 256, fp32 decode; or a problem too large for one launch */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size query */
   ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
 } attn_status_t;
@@ -72,9 +74,9 @@ typedef struct {
   int32_t Tkv;    /* key/value length (KV cache capacity for decode), >= 0 */
   int32_t Hq;     /* query heads, >= 1 */
   int32_t Hkv;    /* key/value heads, >= 1, divides Hq */
-  int32_t D;      /* head_dim: 64 or 128 */
+  int32_t D;      /* head_dim: 32, 64, 128 or 256 (bf16); 32, 64 or 128 (fp32) */
   int32_t dtype;  /* attn_dtype_t of Q, K, V, O, dO, dQ, dK, dV */
-  float scale;    /* softmax scale, finite and >= 0 (e.g. 1/sqrt(D)) */
+  float scale;    /* softmax scale, finite and > 0 (e.g. 1/sqrt(D)) */
   int32_t causal; /* 0 or 1; 1 requires Tq == Tkv */
   const int32_t* kv_lens; /* device int32[B] or NULL (= Tkv for every batch) */
   int32_t window_left;    /* local window: keys down to i - window_left; < 0 = no bound */

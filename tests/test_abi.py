@@ -57,7 +57,7 @@ def validate(p, op=attn.OP_FWD):
     ({"D": 96}, attn.OP_FWD, attn.ATTN_ERR_UNSUPPORTED),
     ({"D": 32}, attn.OP_FWD, attn.ATTN_OK),
     ({"D": 32, "Tq": 16, "Tkv": 4096}, attn.OP_DECODE, attn.ATTN_OK),
-    ({"D": 32, "dtype": attn.ATTN_FP32}, attn.OP_BWD, attn.ATTN_ERR_UNSUPPORTED),
+    ({"D": 32, "dtype": attn.ATTN_FP32}, attn.OP_BWD, attn.ATTN_OK),
     ({"D": 256}, attn.OP_BWD, attn.ATTN_OK),
     ({"D": 256, "Tq": 16, "Tkv": 4096}, attn.OP_DECODE, attn.ATTN_OK),
     ({"D": 256, "dtype": attn.ATTN_FP32}, attn.OP_FWD, attn.ATTN_ERR_UNSUPPORTED),
