@@ -372,6 +372,294 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   }
 }
 
+// dK/dV at head_dim 128 with the work of each 32-key block split over a pair
+// of waves, so that every wave holds half the state (K or V rows, dV or dK)
+// and two waves share each SIMD (the single-role kernel holds both and runs
+// one wave per SIMD; at head_dim 64 and 32 it stays the faster one):
+//   S wave:  K rows (B operand) and dV^T; per 32-row block S = Q K^T,
+//            P = exp2(c S'), P (bf16) to LDS for its partner,
+//            dV^T += dO^T P
+//   dP wave: V rows and dK^T; dP = dO V^T, P from LDS,
+//            dS = P dP', dK^T += Q^T dS
+// Both roles run the same products: in step i the row product (S or dP) of
+// block i + 1 beside the transposed product (dV or dK) of block i, whose B
+// operand (P or dS) came from the previous step. One workgroup barrier per
+// step hands P over (double-buffered); the Q/dO/row-term ring is that of the
+// single-role kernel (three stages of 64-row tiles; the copy of tile t + 2
+// starts at step 2t and must have landed by the end of step 2t + 1).
+template <int D>
+struct DkvPairCfg {
+  static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave pair
+  static constexpr int BM = 64;             // query rows per LDS tile
+  static constexpr int NST = 3;             // LDS stages
+  static constexpr int THREADS = 512;       // 4 S waves, then 4 dP waves
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int R = 4;               // depth of the fragment read-ahead
+  static constexpr int TILE = BM * D;
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
+  using C = DkvPairCfg<D>;
+  constexpr int TB = C::TILE * 2;                 // bytes of one tile
+  constexpr int BB = 32 * D * 2;                  // bytes of one 32-row block
+  constexpr int R_OFF = 0;                        // row terms: 16 bytes per query row
+  constexpr int Q_OFF = C::NST * C::BM * 16;      // Q stages
+  constexpr int G_OFF = Q_OFF + C::NST * TB;      // dO stages
+  constexpr int X_OFF = G_OFF + C::NST * TB;      // P hand-over: [2][4 waves][2 halves][64 lanes] x 16 B
+  constexpr int XB = 4 * 2 * 1024;                // bytes of one hand-over buffer
+  __shared__ __attribute__((aligned(16))) char smem[X_OFF + 2 * XB];
+  uint16_t* const q_st = (uint16_t*)(smem + Q_OFF);
+  uint16_t* const g_st = (uint16_t*)(smem + G_OFF);
+  uint16_t* const r_st = (uint16_t*)(smem + R_OFF);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2;                // 0: S, P, dV; 1: dP, dS, dK
+  const int w4 = wave & 3;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = bid % a.num_ktiles;
+  int rest = bid / a.num_ktiles;
+  const int kh = rest % a.Hkv;
+  rest /= a.Hkv;
+  const int b = rest % a.B;
+  const int split = rest / a.B;
+  const int G = a.Hq / a.Hkv;
+  const int h_lo = split * a.heads_per_split;
+  const int nh = min(a.heads_per_split, G - h_lo);
+  const int k0 = kt * C::BN;
+  const int key = k0 + 32 * w4 + l32;
+
+  const long krs = (long)a.Hkv * D;
+  const long qrs = (long)a.Hq * D;
+  const long kvoff = ((long)b * a.Tkv * a.Hkv + kh) * D;
+  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
+
+  f32x16_t acc[C::DB];  // dV^T (S wave) or dK^T (dP wave)
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) acc[i] = f32x16_t{};
+
+  const int kmax = min(k0 + C::BN, kvlim) - 1;
+  int i_lo = a.causal ? k0 : 0;
+  if (a.win_right >= 0) i_lo = max(i_lo, k0 - a.win_right);
+  int i_hi = a.Tq - 1;
+  if (a.win_left >= 0) i_hi = min(i_hi, kmax + a.win_left);
+  const int qt_begin = i_lo / C::BM;
+  const int nq = i_hi >= i_lo ? i_hi / C::BM + 1 - qt_begin : 0;
+  const int ntiles = nh * nq;
+
+  if (k0 < kvlim && ntiles > 0) {
+    // K (S wave) or V (dP wave) rows of this lane's key as B operands.
+    u32x4_t frag[C::KS];
+    const bool key_ok = key < kvlim;
+    const uint16_t* src = role == 0 ? (const uint16_t*)a.k : (const uint16_t*)a.v;
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t)
+      frag[t] = key_ok ? gload16(src + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    const float c = a.scale_log2;
+    const int tr_row = 4 * hh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int wave_min_key = k0 + 32 * w4;
+    const int wave_max_key = wave_min_key + 31;
+
+    // Lane byte offsets: the row operand is Q (S wave) or dO (dP wave), the
+    // transposed operand the other one.
+    const uint32_t row_base = role == 0 ? Q_OFF : G_OFF;
+    const uint32_t tr_base = role == 0 ? G_OFF : Q_OFF;
+    uint32_t row_off[C::KS], tr_off[C::DB][2];
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) row_off[t] = row_base + 2 * swz_off<D>(l32, 16 * t + 8 * hh);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      tr_off[db][0] = tr_base + 2 * swz_off<D>(tr_row, 32 * db + tr_col);
+      tr_off[db][1] = tr_base + 2 * swz_off<D>(tr_row + 8, 32 * db + tr_col);
+    }
+    const uint32_t x_off = X_OFF + (w4 * 2 * 64 + lane) * 16;  // + buffer * XB + half * 1024
+
+    const TileCopy<D, C::BM, C::THREADS> qcopy(qrs, tid);
+    auto tile_q0 = [&](int t) { return (qt_begin + t % nq) * C::BM; };
+    auto issue = [&](int t) {
+      const int st = t % C::NST;
+      const int h = kh * G + h_lo + t / nq;
+      const int q0 = tile_q0(t);
+      const long hoff = ((long)b * a.Tq * a.Hq + h) * D;
+      uint16_t* qs = q_st + st * C::TILE;
+      uint16_t* gs = g_st + st * C::TILE;
+      if (q0 + C::BM <= a.Tq) {
+        qcopy.copy(qs, (const uint16_t*)a.q + hoff, qrs, q0);
+        qcopy.copy(gs, (const uint16_t*)a.dout + hoff, qrs, q0);
+      } else {
+        dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
+        dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
+      }
+      static_assert(C::BM == 64, "row terms are copied by one wave of 64 lanes");
+      if (wave == 0) {
+        int i = q0 + lane;
+        i = i < a.Tq ? i : a.Tq - 1;
+        dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
+      }
+    };
+    auto mask_tile = [&](int t) {
+      if (t >= ntiles) return false;
+      const int q0 = tile_q0(t);
+      return (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
+             (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
+    };
+    // Byte offset of block `blk` (32 rows) in its stage.
+    auto blk_off = [&](int blk) { return (uint32_t)(((blk >> 1) % C::NST) * TB + (blk & 1) * BB); };
+
+    // Row terms as one extra k-step (see the single-role kernel): the S wave
+    // selects -LSE/scale, the dP wave -D.
+    const unsigned one2 = 0x3F803F80u, one1 = 0x00003F80u;
+    const u32x4_t sel = hh != 0 ? u32x4_t{0, 0, 0, 0}
+                        : role == 0 ? u32x4_t{one2, one1, 0, 0} : u32x4_t{0, 0, one2, one1};
+
+    // Row product of block blk: S (S wave) or dP (dP wave), row terms included.
+    auto row_product = [&](int blk) {
+      const uint32_t bo = blk_off(blk);
+      const int st = (blk >> 1) % C::NST;
+      const u32x4_t terms = lds_read16((const uint16_t*)(smem + R_OFF + (st * C::BM + 32 * (blk & 1) + l32) * 16));
+      u32x4_t ra[C::R];
+#pragma unroll
+      for (int m = 0; m < C::R; ++m) ra[m] = lds_read16((const uint16_t*)(smem + row_off[m] + bo));
+      f32x16_t r = f32x16_t{};
+#pragma unroll
+      for (int m = 0; m < C::KS; ++m) {
+        r = mfma_bf16(ra[m % C::R], frag[m], r);
+        if (m + C::R < C::KS) ra[m % C::R] = lds_read16((const uint16_t*)(smem + row_off[m + C::R] + bo));
+      }
+      return mfma_bf16(terms, sel, r);
+    };
+    // Transposed product of block blk: acc += (dO or Q)^T x packed B operand.
+    auto tr_product = [&](int blk, const u32x4_t (&pk)[2]) {
+      const uint32_t bo = blk_off(blk);
+      u32x2_t tra[C::R][2];
+      auto rd = [&](int m, int slot) {
+        const int u = m / C::DB, db = m % C::DB;
+        tra[slot][0] = lds_read_tr((const uint16_t*)(smem + tr_off[db][0] + bo + 16 * u * D * 2));
+        tra[slot][1] = lds_read_tr((const uint16_t*)(smem + tr_off[db][1] + bo + 16 * u * D * 2));
+      };
+#pragma unroll
+      for (int m = 0; m < C::R; ++m) rd(m, m);
+#pragma unroll
+      for (int m = 0; m < C::KS; ++m) {
+        const int u = m / C::DB, db = m % C::DB, slot = m % C::R;
+        acc[db] = mfma_bf16(u32x4_t{tra[slot][0][0], tra[slot][0][1], tra[slot][1][0], tra[slot][1][1]}, pk[u],
+                            acc[db]);
+        if (m + C::R < C::KS) rd(m + C::R, slot);
+      }
+    };
+    auto pack8 = [](const float* v) {
+      return u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+    };
+
+    issue(0);
+    if (ntiles > 1) issue(1);
+    wait_vmem();
+    __syncthreads();
+    const int nb = 2 * ntiles;  // 32-row blocks
+    // Ring bookkeeping shared by both roles (same barriers in the same order).
+    auto step_end = [&](int i) {
+      if (i & 1) wait_vmem();  // the tile issued at step i - 1 has landed
+      __syncthreads();
+    };
+    auto step_begin = [&](int i) {
+      if ((i & 1) == 0 && i / 2 + 2 < ntiles) issue(i / 2 + 2);
+    };
+
+    if (role == 0) {
+      // P of block blk: exp2 of the row product, masked, packed, handed over.
+      u32x4_t pk[2];
+      auto softmax = [&](int blk, const f32x16_t& s) {
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(s[r] * c);
+        if (mask_tile(blk >> 1)) {
+          const int q0 = tile_q0(blk >> 1) + 32 * (blk & 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ql = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = (key >= key_lo(ql, a.win_left)) & (key <= key_hi(ql, kvlim, a.causal, a.win_right)) &
+                            (ql < a.Tq);
+            pv[r] = ok ? pv[r] : 0.f;
+          }
+        }
+        pk[0] = pack8(pv);
+        pk[1] = pack8(pv + 8);
+        const uint32_t xo = x_off + (blk & 1) * XB;
+        lds_write16((uint16_t*)(smem + xo), pk[0]);
+        lds_write16((uint16_t*)(smem + xo + 1024), pk[1]);
+      };
+      softmax(0, row_product(0));
+      __syncthreads();
+      for (int i = 0; i < nb; ++i) {
+        step_begin(i);
+        const f32x16_t s = row_product(i + 1);
+        tr_product(i, pk);
+        softmax(i + 1, s);
+        step_end(i);
+      }
+    } else {
+      f32x16_t dp = row_product(0);
+      __syncthreads();
+      for (int i = 0; i < nb; ++i) {
+        step_begin(i);
+        // dS of block i from the handed-over P and the previous step's dP'.
+        const uint32_t xo = x_off + (i & 1) * XB;
+        const u32x4_t p0 = lds_read16((const uint16_t*)(smem + xo));
+        const u32x4_t p1 = lds_read16((const uint16_t*)(smem + xo + 1024));
+        float dsv[16];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          dsv[2 * w] = bf16_lo(p0[w]) * dp[2 * w];
+          dsv[2 * w + 1] = bf16_hi(p0[w]) * dp[2 * w + 1];
+          dsv[8 + 2 * w] = bf16_lo(p1[w]) * dp[8 + 2 * w];
+          dsv[8 + 2 * w + 1] = bf16_hi(p1[w]) * dp[8 + 2 * w + 1];
+        }
+        const u32x4_t pk[2] = {pack8(dsv), pack8(dsv + 8)};
+        dp = row_product(i + 1);
+        tr_product(i, pk);
+        step_end(i);
+      }
+    }
+  }
+
+  // Store: lane = key, register r of block db = head_dim 32*db + 8*(r/4) + 4*hh + r%4;
+  // the S wave holds dV, the dP wave dK.
+  const bool is_dk = role == 1;
+  if (a.kv_split > 1) {
+    if (key < a.Tkv) {
+      const long part = (long)a.B * a.Tkv * krs;
+      float* dst = a.dkv_part + (is_dk ? split : a.kv_split + split) * part + kvoff + key * krs;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * hh;
+          *(f32x4_t*)(dst + d) = f32x4_t{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+        }
+    }
+    return;
+  }
+  if (key < a.Tkv) {
+    const float f = is_dk ? a.scale : 1.f;
+    uint16_t* dst = (uint16_t*)(is_dk ? a.dk : a.dv) + kvoff + key * krs;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hh;
+        *(u32x2_t*)(dst + d) = u32x2_t{pack_bf16(acc[db][4 * g] * f, acc[db][4 * g + 1] * f),
+                                       pack_bf16(acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f)};
+      }
+  }
+}
+
 // dK/dV at head_dim 256. The accumulators of all 256 columns would take 256
 // registers per lane besides K and V (128), so each workgroup forms one
 // 128-column half of dK and dV (S and dP are recomputed per half), and a
@@ -895,6 +1183,8 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
     if (kblocks > 0) {
       if constexpr (D == 256)
         hipLaunchKernelGGL(attn_dkdv_d256_kernel, dim3((unsigned)(2 * kblocks)), dim3(DkvWideCfg::THREADS), 0, s, a);
+      else if constexpr (D == 128)
+        hipLaunchKernelGGL(attn_dkdv_pair_kernel<D>, dim3((unsigned)kblocks), dim3(DkvPairCfg<D>::THREADS), 0, s, a);
       else
         hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(DkvCfg<D>::THREADS), 0, s, a);
       if (a.kv_split > 1) {
