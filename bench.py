@@ -66,6 +66,9 @@ def parse_args():
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 CSV output (kernel-trace stats, FETCH_SIZE pass, WRITE_SIZE pass) into "
                          "the summaries under profiles/ and exit (no GPU use)")
+    ap.add_argument("--summarize-fp32", metavar="STATS_DIR",
+                    help="turn a rocprofv3 kernel trace of the fp32 suite into profiles/fp32_grid_kernel_stats.md "
+                         "and exit (no GPU use); --profile-command records the command")
     ap.add_argument("--profile-command", default="", help="kernel-trace command recorded in the summaries")
     ap.add_argument("--counter-command", default="", help="counter-pass command recorded in the summaries")
     ap.add_argument("--mfma-dir", default="", help="with --summarize: rocprofv3 output of a pass with "
@@ -209,6 +212,59 @@ def summarize(stats_dir, fetch_dir, write_dir, command, counter_command):
         json.dump({"source_digest": source_digest(), "command": counter_command,
                    "kernels": {k: {"bytes_per_launch": round(v)} for k, v in traffic.items()}}, f, indent=1)
     print(f"wrote summaries under {prof}")
+
+
+def summarize_fp32(stats_dir, command):
+    """Per-kernel, per-grid durations of a kernel trace of the fp32 suite (B4 H8, head_dim 64/128)."""
+    import csv
+    import glob
+    from forward_backward_amd.inputs import workload_cases
+    from forward_backward_amd.metrics import attention_flops
+
+    runs = {}
+    for path in glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            name = _short_name(r["Kernel_Name"])
+            if "f32_kernel" not in name:
+                continue
+            grid = int(r["Grid_Size_X"]) if "Grid_Size_X" in r else int(r["Grid_Size"])
+            runs.setdefault((name, grid), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    # Grid (threads) of each kernel per case, to name the shape and price the launch.
+    shapes = {}
+    for c in workload_cases(8):
+        fwd_f = attention_flops(c.B, c.Hq, c.Tq, c.Tkv, c.D, c.causal, "fwd")
+        nq, nk = -(-c.Tq // 128), -(-c.Tkv // 128)
+        for kern, grid, fl in ((f"attn_fwd_f32_kernel<{c.D}>", 256 * nq * c.Hq * c.B, fwd_f),
+                               (f"attn_dq_f32_kernel<{c.D}>", 256 * nq * c.Hq * c.B, 1.5 * fwd_f),
+                               (f"attn_dkdv_f32_kernel<{c.D}>", 256 * nk * c.Hkv * c.B, 2 * fwd_f)):
+            shapes.setdefault((kern, grid), []).append((c, fl))
+    lines = ["# fp32 kernels on the fp32 matrix cores: the fp32 grid (B4 H8, head_dim 64/128)", "",
+             "rocprofv3 kernel trace of the command below (each shape timed non-causal, then causal; a grid "
+             "covers both). TFLOP/s = the launch's algorithmic FLOPs (forward 4, dK/dV 8, dQ 6 x B H Tq Tkv D, "
+             "halved when causal) / median duration; peak 157.3 TFLOP/s (fp32 matrix).", "",
+             "```", command or "(command not recorded)", "```", "",
+             "| kernel | grid (threads) | shape | dispatches | median us | TFLOP/s | of fp32 peak |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid), ds in sorted(runs.items()):
+        cases = shapes.get((name, grid), [])
+        ds = [d for _, d in sorted(ds)]
+        # Both cases of a shape share the grid; the suite runs the non-causal one first, with as many
+        # dispatches as the causal one.
+        halves = [("full", ds[:len(ds) // 2]), ("causal", ds[len(ds) // 2:])] if len(cases) == 2 else [("", ds)]
+        for tag, part in halves:
+            if not part:
+                continue
+            med = sorted(part)[len(part) // 2]
+            case = next((c for c, _ in cases if (tag == "causal") == c.causal), None) if cases else None
+            fl = next((f for c, f in cases if case is not None and c is case), None)
+            tf = f"{fl / (med * 1e-9) / 1e12:.1f}" if fl else ""
+            frac = f"{fl / (med * 1e-9) / 1e12 / 157.3:.0%}" if fl else ""
+            lines.append(f"| `{name}` | {grid} | {case.name if case else '?'} | {len(part)} | {med / 1e3:.1f} | "
+                         f"{tf} | {frac} |")
+    with open(os.path.join(ROOT, "profiles", "fp32_grid_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/fp32_grid_kernel_stats.md")
 
 
 def summarize_mfma(stats_dir, mfma_dir, command, profile_command):
@@ -624,6 +680,9 @@ def cpu_baseline(case, seconds):
 
 def main():
     args = parse_args()
+    if args.summarize_fp32:
+        summarize_fp32(args.summarize_fp32, args.profile_command)
+        return
     if args.summarize:
         summarize(*args.summarize, args.profile_command, args.counter_command)
         if args.mfma_dir:
