@@ -1174,6 +1174,203 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   }
 }
 
+// dQ with the two 32-key blocks of each tile split over a pair of waves that
+// share the same 32 query rows: wave w takes block 0 and wave w + 4 block 1 of
+// every tile, each with its own dQ^T partial, and the pair adds the two
+// partials in that order at the end (deterministic). Without the two-block
+// software pipeline of the single-pair kernel a wave needs well under 256
+// registers, so two waves share each SIMD. Per block: S^T = K Q^T and
+// dP^T = V dO^T (lane = query row), dS^T = P (dP - D), dQ^T += K^T dS^T.
+template <int D>
+struct DqPairCfg {
+  static constexpr int BM = 128;            // query rows, 32 per wave pair
+  static constexpr int BN = 64;             // keys per tile (one 32-key block per wave of a pair)
+  static constexpr int THREADS = 512;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int R = 2;               // depth of the fragment read-ahead
+  static constexpr int TILE = BN * D;
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
+  using C = DqPairCfg<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * C::TILE];  // stage s: K at 2s, V at 2s + 1
+  static_assert(4 * C::TILE * 2 >= 4 * 64 * 16 * C::DB * 4, "the partial hand-over reuses the tiles");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2;               // key block of each tile
+  const int w4 = wave & 3;                  // row block
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int nqt = (a.Tq + C::BM - 1) / C::BM;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = nqt - 1 - (bid % nqt);
+  const int bh = bid / nqt;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+  const int kh = h / (a.Hq / a.Hkv);
+  const int q0 = qt * C::BM;
+
+  const long qrs = (long)a.Hq * D;
+  const long krs = (long)a.Hkv * D;
+  const long qoff = ((long)b * a.Tq * a.Hq + h) * D;
+  const uint16_t* kb = (const uint16_t*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
+  const uint16_t* vb = (const uint16_t*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
+
+  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
+  const int kv_first = key_lo(q0, a.win_left);
+  const int kv_end = key_hi(q0 + C::BM - 1, kvlim, a.causal, a.win_right) + 1;
+  const int j0 = kv_first / C::BN;
+  const int ntiles = kv_end > kv_first ? (kv_end + C::BN - 1) / C::BN - j0 : 0;
+
+  const int qrow = q0 + 32 * w4 + l32;
+  const bool row_ok = qrow < a.Tq;
+  u32x4_t qf[C::KS], gf[C::KS];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) {
+    qf[t] = row_ok ? gload16((const uint16_t*)a.q + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    gf[t] = row_ok ? gload16((const uint16_t*)a.dout + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+  }
+  const long stat = ((long)b * a.Hq + h) * a.Tq + qrow;
+  const float lse2 = row_ok ? a.lse2[stat] : INFINITY;
+  const float dlt = row_ok ? a.delta[stat] : 0.f;
+  const float c = a.scale_log2;
+
+  f32x16_t acc[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) acc[i] = f32x16_t{};
+
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int wave_min_row = q0 + 32 * w4;
+  const int row_lo = key_lo(qrow, a.win_left);
+  const int row_hi = key_hi(qrow, kvlim, a.causal, a.win_right);
+  const int wave_all_lo = key_lo(wave_min_row + 31, a.win_left);
+  const int wave_all_hi = key_hi(wave_min_row, kvlim, a.causal, a.win_right);
+  // Lane offsets (elements) inside a stage, for this wave's key block.
+  int nrm[C::KS], trd[C::DB][2];
+#pragma unroll
+  for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh) + 32 * half * D;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    trd[db][0] = swz_off<D>(tr_row, 32 * db + tr_col) + 32 * half * D;
+    trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col) + 32 * half * D;
+  }
+
+  auto issue = [&](int it) {
+    uint16_t* ks = tiles + (it & 1) * 2 * C::TILE;
+    const int k0 = (j0 + it) * C::BN;
+    dma_tile<D, C::BN, C::THREADS, true>(ks, kb, krs, k0, kv_end, tid);
+    dma_tile<D, C::BN, C::THREADS, true>(ks + C::TILE, vb, krs, k0, kv_end, tid);
+  };
+
+  // One 32-key block: S^T, dP^T, the masked dS^T, then dQ^T += K^T dS^T. The
+  // element-wise mask is a select-only fix-up under a uniform branch (a
+  // branch between two whole block bodies made the register allocator copy
+  // the accumulators).
+  auto block = [&](bool mask, const uint16_t* kl, const uint16_t* vl, int kblk0) {
+    u32x4_t ka[C::R], va[C::R];
+#pragma unroll
+    for (int m = 0; m < C::R; ++m) {
+      ka[m] = lds_read16(kl + nrm[m]);
+      va[m] = lds_read16(vl + nrm[m]);
+    }
+    f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t) {
+      s = mfma_bf16(ka[t % C::R], qf[t], s);
+      dp = mfma_bf16(va[t % C::R], gf[t], dp);
+      if (t + C::R < C::KS) {
+        ka[t % C::R] = lds_read16(kl + nrm[t + C::R]);
+        va[t % C::R] = lds_read16(vl + nrm[t + C::R]);
+      }
+    }
+    u32x2_t kt[1][C::DB][2];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      kt[0][db][0] = lds_read_tr(kl + trd[db][0]);
+      kt[0][db][1] = lds_read_tr(kl + trd[db][1]);
+    }
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+    if (mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kblk0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        pv[r] = (key >= row_lo) & (key <= row_hi) ? pv[r] : 0.f;
+      }
+    }
+    u32x4_t dsb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float dsv[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) dsv[x] = pv[8 * u + x] * (dp[8 * u + x] - dlt);
+      dsb[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
+                       pack_bf16(dsv[6], dsv[7])};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          kt[0][db][0] = lds_read_tr(kl + 16 * D + trd[db][0]);
+          kt[0][db][1] = lds_read_tr(kl + 16 * D + trd[db][1]);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        acc[db] = mfma_bf16(u32x4_t{kt[0][db][0][0], kt[0][db][0][1], kt[0][db][1][0], kt[0][db][1][1]}, dsb[u],
+                            acc[db]);
+    }
+  };
+
+  if (ntiles > 0) issue(0);
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vmem();
+    __syncthreads();  // tile it landed; every wave is done with tile it - 1
+    if (it + 1 < ntiles) issue(it + 1);
+    const uint16_t* kl = tiles + (it & 1) * 2 * C::TILE;
+    const int k0 = (j0 + it) * C::BN;
+    const int kblk0 = k0 + 32 * half;
+    const bool mask = (kblk0 < wave_all_lo) || (kblk0 + 31 > wave_all_hi);
+    block(mask, kl, kl + C::TILE, kblk0);
+  }
+
+  // The pair's partials: block-1 waves hand theirs over through LDS, block-0
+  // waves add them (block 0 + block 1) and store.
+  __syncthreads();
+  float* xf = reinterpret_cast<float*>(tiles) + w4 * (16 * C::DB * 64);
+  if (half == 1) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xf[(16 * db + r) * 64 + lane] = acc[db][r];
+  }
+  __syncthreads();
+  if (half == 0 && row_ok) {
+    uint16_t* dqp = (uint16_t*)a.dq + qoff + qrow * qrs;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * g + x;
+          v[x] = (acc[db][r] + xf[(16 * db + r) * 64 + lane]) * a.scale;
+        }
+        const int d = 32 * db + 8 * g + 4 * hh;
+        *(u32x2_t*)(dqp + d) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      }
+  }
+}
+
 template <int D>
 void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
   if (pass == kBwdPre) {
@@ -1195,7 +1392,12 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
   } else {
     const long nqt = (a.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
     const long qblocks = nqt * a.Hq * a.B;
-    if (qblocks > 0) hipLaunchKernelGGL(attn_dq_bf16_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
+    if (qblocks > 0) {
+      if constexpr (D == 64 || D == 128)
+        hipLaunchKernelGGL(attn_dq_pair_kernel<D>, dim3((unsigned)qblocks), dim3(DqPairCfg<D>::THREADS), 0, s, a);
+      else
+        hipLaunchKernelGGL(attn_dq_bf16_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, a);
+    }
   }
 }
 
