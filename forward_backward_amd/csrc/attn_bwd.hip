@@ -372,10 +372,12 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   }
 }
 
-// dK/dV at head_dim 128 with the work of each 32-key block split over a pair
-// of waves, so that every wave holds half the state (K or V rows, dV or dK)
-// and two waves share each SIMD (the single-role kernel holds both and runs
-// one wave per SIMD; at head_dim 64 and 32 it stays the faster one):
+// dK/dV at head_dim 128 and 256 with the work of each 32-key block split over
+// a pair of waves, so that every wave holds half the state (K or V rows, dV or
+// dK): at head_dim 128 two waves share each SIMD (the single-role kernel holds
+// both and runs one wave per SIMD; at head_dim 64 and 32 it stays the faster
+// one); at head_dim 256 one wave per SIMD holds all 256 columns of its dV or
+// dK, so S and dP are formed once per block:
 //   S wave:  K rows (B operand) and dV^T; per 32-row block S = Q K^T,
 //            P = exp2(c S'), P (bf16) to LDS for its partner,
 //            dV^T += dO^T P
@@ -389,26 +391,39 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
 // starts at step 2t and must have landed by the end of step 2t + 1).
 template <int D>
 struct DkvPairCfg {
-  static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave pair
-  static constexpr int BM = 64;             // query rows per LDS tile
-  static constexpr int NST = 3;             // LDS stages
-  static constexpr int THREADS = 512;       // 4 S waves, then 4 dP waves
+  // head_dim 128: 4 pairs (two waves per SIMD), 64-row tiles, 3 stages.
+  // head_dim 256: 2 pairs (one wave per SIMD: a wave holds 64 registers of K
+  // or V and 128 of dV or dK), 32-row tiles, 4 stages.
+  static constexpr int NP = D > 128 ? 2 : 4;        // wave pairs, 32 keys each
+  static constexpr int BN = 32 * NP;                // keys per workgroup
+  static constexpr int BM = D > 128 ? 32 : 64;      // query rows per LDS tile
+  static constexpr int BPT = BM / 32;               // 32-row blocks per tile
+  static constexpr int NST = D > 128 ? 4 : 3;       // LDS stages
+  static constexpr int THREADS = 128 * NP;          // NP S waves, then NP dP waves
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int R = 4;               // depth of the fragment read-ahead
+  static constexpr int R = 4;                       // depth of the fragment read-ahead
   static constexpr int TILE = BM * D;
+  static_assert(kBwdBlockN % BN == 0, "a 128-key tile splits into whole workgroups");
 };
 
+// s_waitcnt vmcnt(N), the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int D>
-__global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
+__global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(BwdArgs a) {
   using C = DkvPairCfg<D>;
   constexpr int TB = C::TILE * 2;                 // bytes of one tile
   constexpr int BB = 32 * D * 2;                  // bytes of one 32-row block
   constexpr int R_OFF = 0;                        // row terms: 16 bytes per query row
   constexpr int Q_OFF = C::NST * C::BM * 16;      // Q stages
   constexpr int G_OFF = Q_OFF + C::NST * TB;      // dO stages
-  constexpr int X_OFF = G_OFF + C::NST * TB;      // P hand-over: [2][4 waves][2 halves][64 lanes] x 16 B
-  constexpr int XB = 4 * 2 * 1024;                // bytes of one hand-over buffer
+  constexpr int X_OFF = G_OFF + C::NST * TB;      // P hand-over: [2][NP waves][2 halves][64 lanes] x 16 B
+  constexpr int XB = C::NP * 2 * 1024;            // bytes of one hand-over buffer
   __shared__ __attribute__((aligned(16))) char smem[X_OFF + 2 * XB];
   uint16_t* const q_st = (uint16_t*)(smem + Q_OFF);
   uint16_t* const g_st = (uint16_t*)(smem + G_OFF);
@@ -417,14 +432,15 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int role = wave >> 2;                // 0: S, P, dV; 1: dP, dS, dK
-  const int w4 = wave & 3;
+  const int role = wave / C::NP;              // 0: S, P, dV; 1: dP, dS, dK
+  const int w4 = wave % C::NP;               // key block of the pair
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = bid % a.num_ktiles;
-  int rest = bid / a.num_ktiles;
+  const int nkt = a.num_ktiles * (kBwdBlockN / C::BN);  // workgroups per (batch, KV head, split)
+  const int kt = bid % nkt;
+  int rest = bid / nkt;
   const int kh = rest % a.Hkv;
   rest /= a.Hkv;
   const int b = rest % a.B;
@@ -479,7 +495,7 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
       tr_off[db][0] = tr_base + 2 * swz_off<D>(tr_row, 32 * db + tr_col);
       tr_off[db][1] = tr_base + 2 * swz_off<D>(tr_row + 8, 32 * db + tr_col);
     }
-    const uint32_t x_off = X_OFF + (w4 * 2 * 64 + lane) * 16;  // + buffer * XB + half * 1024
+    const uint32_t x_off = X_OFF + (w4 * 2 * 64 + lane) * 16;  // + buffer * XB + half * 1024 (XB per buffer)
 
     const TileCopy<D, C::BM, C::THREADS> qcopy(qrs, tid);
     auto tile_q0 = [&](int t) { return (qt_begin + t % nq) * C::BM; };
@@ -497,8 +513,8 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
         dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
         dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
       }
-      static_assert(C::BM == 64, "row terms are copied by one wave of 64 lanes");
-      if (wave == 0) {
+      // Row terms: one 16-byte row per lane of wave 0 (one copy instruction).
+      if (wave == 0 && lane < C::BM) {
         int i = q0 + lane;
         i = i < a.Tq ? i : a.Tq - 1;
         dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
@@ -510,8 +526,8 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
       return (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
              (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
     };
-    // Byte offset of block `blk` (32 rows) in its stage.
-    auto blk_off = [&](int blk) { return (uint32_t)(((blk >> 1) % C::NST) * TB + (blk & 1) * BB); };
+    // Byte offset of block `blk` (32 rows): its tile's stage and its place in the tile.
+    auto blk_off = [&](int blk) { return (uint32_t)(((blk / C::BPT) % C::NST) * TB + (blk % C::BPT) * BB); };
 
     // Row terms as one extra k-step (see the single-role kernel): the S wave
     // selects -LSE/scale, the dP wave -D.
@@ -522,8 +538,9 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
     // Row product of block blk: S (S wave) or dP (dP wave), row terms included.
     auto row_product = [&](int blk) {
       const uint32_t bo = blk_off(blk);
-      const int st = (blk >> 1) % C::NST;
-      const u32x4_t terms = lds_read16((const uint16_t*)(smem + R_OFF + (st * C::BM + 32 * (blk & 1) + l32) * 16));
+      const int st = (blk / C::BPT) % C::NST;
+      const u32x4_t terms =
+          lds_read16((const uint16_t*)(smem + R_OFF + (st * C::BM + 32 * (blk % C::BPT) + l32) * 16));
       u32x4_t ra[C::R];
 #pragma unroll
       for (int m = 0; m < C::R; ++m) ra[m] = lds_read16((const uint16_t*)(smem + row_off[m] + bo));
@@ -558,18 +575,36 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
       return u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
     };
 
-    issue(0);
-    if (ntiles > 1) issue(1);
+    for (int t = 0; t < C::NST - 1 && t < ntiles; ++t) issue(t);
     wait_vmem();
     __syncthreads();
-    const int nb = 2 * ntiles;  // 32-row blocks
+    const int nb = C::BPT * ntiles;  // 32-row blocks
     // Ring bookkeeping shared by both roles (same barriers in the same order).
-    auto step_end = [&](int i) {
-      if (i & 1) wait_vmem();  // the tile issued at step i - 1 has landed
-      __syncthreads();
-    };
+    // Step i reads blocks i and i + 1, so tile u (blocks BPT u ..) is read in
+    // steps BPT u - 1 .. BPT u + BPT - 1. At the first step of tile t, tile
+    // t - 1 has been read for the last time and tile t - 1 + NST takes its
+    // stage: three steps (BPT 2, NST 3) or two (BPT 1, NST 4) before its
+    // first use, and the waits below make it land in time.
     auto step_begin = [&](int i) {
-      if ((i & 1) == 0 && i / 2 + 2 < ntiles) issue(i / 2 + 2);
+      if (i % C::BPT == 0 && i / C::BPT - 1 + C::NST < ntiles) issue(i / C::BPT - 1 + C::NST);
+    };
+    auto step_end = [&](int i) {
+      if constexpr (C::BPT == 2) {
+        if (i & 1) wait_vmem();  // the tile issued at step i - 1 has landed
+      } else {
+        // Tile i + 2 (issued at step i - 1) must land; the copies of tile i + 3
+        // issued at this step may stay in flight.
+        constexpr int CP = 2 * TileCopy<D, C::BM, C::THREADS>::ITERS;  // copy instructions per wave and tile
+        if (i + 3 < ntiles) {
+          if (wave == 0)
+            wait_vmcnt<CP + 1>();
+          else
+            wait_vmcnt<CP>();
+        } else {
+          wait_vmem();
+        }
+      }
+      __syncthreads();
     };
 
     if (role == 0) {
@@ -579,8 +614,8 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(s[r] * c);
-        if (mask_tile(blk >> 1)) {
-          const int q0 = tile_q0(blk >> 1) + 32 * (blk & 1);
+        if (mask_tile(blk / C::BPT)) {
+          const int q0 = tile_q0(blk / C::BPT) + 32 * (blk % C::BPT);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -660,226 +695,6 @@ __global__ __launch_bounds__(512) void attn_dkdv_pair_kernel(BwdArgs a) {
   }
 }
 
-// dK/dV at head_dim 256. The accumulators of all 256 columns would take 256
-// registers per lane besides K and V (128), so each workgroup forms one
-// 128-column half of dK and dV (S and dP are recomputed per half), and a
-// 64-row tile of Q and dO (32 KiB each) would overfill the LDS with three
-// stages; this variant walks 32-row tiles through a two-stage ring without
-// the cross-block pipeline: per tile S, dP (with the row terms), the masked
-// softmax, then the dV/dK products of the half.
-struct DkvWideCfg {
-  static constexpr int D = 256;
-  static constexpr int HALF = 128;          // dK/dV columns per workgroup
-  static constexpr int BN = kBwdBlockN;     // 128 keys, 32 per wave
-  static constexpr int BM = 32;             // query rows per tile
-  static constexpr int THREADS = 256;
-  static constexpr int KS = D / 16;
-  static constexpr int DBH = HALF / 32;
-  static constexpr int TILE = BM * D;
-};
-
-__global__ __launch_bounds__(256) void attn_dkdv_d256_kernel(BwdArgs a) {
-  using C = DkvWideCfg;
-  constexpr int D = C::D;
-  constexpr int TB = C::TILE * 2;
-  constexpr int R_OFF = 0;                  // row terms: 16 bytes per query row, two stages
-  constexpr int Q_OFF = 2 * C::BM * 16;
-  constexpr int G_OFF = Q_OFF + 2 * TB;
-  __shared__ __attribute__((aligned(16))) char smem[G_OFF + 2 * TB];
-  uint16_t* const q_st = (uint16_t*)(smem + Q_OFF);
-  uint16_t* const g_st = (uint16_t*)(smem + G_OFF);
-  uint16_t* const r_st = (uint16_t*)(smem + R_OFF);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = bid % a.num_ktiles;
-  int rest = bid / a.num_ktiles;
-  const int ch = rest % 2;                   // column half of dK/dV
-  rest /= 2;
-  const int kh = rest % a.Hkv;
-  rest /= a.Hkv;
-  const int b = rest % a.B;
-  const int split = rest / a.B;
-  const int G = a.Hq / a.Hkv;
-  const int h_lo = split * a.heads_per_split;
-  const int nh = min(a.heads_per_split, G - h_lo);
-  const int k0 = kt * C::BN;
-  const int key = k0 + 32 * wave + l32;
-
-  const long krs = (long)a.Hkv * D;
-  const long qrs = (long)a.Hq * D;
-  const long kvoff = ((long)b * a.Tkv * a.Hkv + kh) * D;
-  const int kvlim = clamp_len(a.kv_lens, b, a.Tkv);
-
-  f32x16_t dk[C::DBH], dv[C::DBH];
-#pragma unroll
-  for (int i = 0; i < C::DBH; ++i) {
-    dk[i] = f32x16_t{};
-    dv[i] = f32x16_t{};
-  }
-
-  const int kmax = min(k0 + C::BN, kvlim) - 1;
-  int i_lo = a.causal ? k0 : 0;
-  if (a.win_right >= 0) i_lo = max(i_lo, k0 - a.win_right);
-  int i_hi = a.Tq - 1;
-  if (a.win_left >= 0) i_hi = min(i_hi, kmax + a.win_left);
-  const int qt_begin = i_lo / C::BM;
-  const int nq = i_hi >= i_lo ? i_hi / C::BM + 1 - qt_begin : 0;
-  const int ntiles = nh * nq;
-
-  if (k0 < kvlim && ntiles > 0) {
-    u32x4_t kf[C::KS], vf[C::KS];
-    const bool key_ok = key < kvlim;
-#pragma unroll
-    for (int t = 0; t < C::KS; ++t) {
-      kf[t] = key_ok ? gload16((const uint16_t*)a.k + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
-      vf[t] = key_ok ? gload16((const uint16_t*)a.v + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
-    }
-    const float c = a.scale_log2;
-    const int tr_row = 4 * hh + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int wave_min_key = k0 + 32 * wave;
-    const int wave_max_key = wave_min_key + 31;
-    int nrm[C::KS], trd[C::DBH][2];
-#pragma unroll
-    for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
-#pragma unroll
-    for (int db = 0; db < C::DBH; ++db) {
-      trd[db][0] = swz_off<D>(tr_row, C::HALF * ch + 32 * db + tr_col);
-      trd[db][1] = swz_off<D>(tr_row + 8, C::HALF * ch + 32 * db + tr_col);
-    }
-    const unsigned one2 = 0x3F803F80u, one1 = 0x00003F80u;
-    const u32x4_t sel_s = hh == 0 ? u32x4_t{one2, one1, 0, 0} : u32x4_t{0, 0, 0, 0};
-    const u32x4_t sel_d = hh == 0 ? u32x4_t{0, 0, one2, one1} : u32x4_t{0, 0, 0, 0};
-
-    auto tile_q0 = [&](int t) { return (qt_begin + t % nq) * C::BM; };
-    auto issue = [&](int t, int st) {
-      const int h = kh * G + h_lo + t / nq;
-      const int q0 = tile_q0(t);
-      const long hoff = ((long)b * a.Tq * a.Hq + h) * D;
-      dma_tile<D, C::BM, C::THREADS>(q_st + st * C::TILE, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
-      dma_tile<D, C::BM, C::THREADS>(g_st + st * C::TILE, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);
-      if (wave == 0 && lane < C::BM) {
-        int i = q0 + lane;
-        i = i < a.Tq ? i : a.Tq - 1;
-        dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
-      }
-    };
-
-    auto tile = [&](int t, int st) {
-      const int q0 = tile_q0(t);
-      const bool mask = (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
-                        (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
-      const uint16_t* qs = q_st + st * C::TILE;
-      const uint16_t* gs = g_st + st * C::TILE;
-      // S and dP with the row terms (-LSE/scale, -D) through one extra k-step.
-      u32x4_t qa[2], ga[2];
-      qa[0] = lds_read16(qs + nrm[0]);
-      ga[0] = lds_read16(gs + nrm[0]);
-      qa[1] = lds_read16(qs + nrm[1]);
-      ga[1] = lds_read16(gs + nrm[1]);
-      f32x16_t sv = f32x16_t{}, dp = f32x16_t{};
-#pragma unroll
-      for (int m = 0; m < C::KS; ++m) {
-        sv = mfma_bf16(qa[m & 1], kf[m], sv);
-        dp = mfma_bf16(ga[m & 1], vf[m], dp);
-        if (m + 2 < C::KS) {
-          qa[m & 1] = lds_read16(qs + nrm[m + 2]);
-          ga[m & 1] = lds_read16(gs + nrm[m + 2]);
-        }
-      }
-      const u32x4_t terms = lds_read16(r_st + (st * C::BM + l32) * 8);
-      sv = mfma_bf16(terms, sel_s, sv);
-      dp = mfma_bf16(terms, sel_d, dp);
-      u32x4_t pk_p[2], pk_d[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float pv[8], dsv[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int r = 8 * u + x;
-          const float p = fast_exp2(sv[r] * c);
-          pv[x] = p;
-          dsv[x] = p * dp[r];
-        }
-        if (mask) {
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int r = 8 * u + x;
-            const int ql = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = (key >= key_lo(ql, a.win_left)) &
-                            (key <= key_hi(ql, kvlim, a.causal, a.win_right)) & (ql < a.Tq);
-            pv[x] = ok ? pv[x] : 0.f;
-            dsv[x] = ok ? dsv[x] : 0.f;
-          }
-        }
-        pk_p[u] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
-                          pack_bf16(pv[6], pv[7])};
-        pk_d[u] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]), pack_bf16(dsv[4], dsv[5]),
-                          pack_bf16(dsv[6], dsv[7])};
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS over this half's columns.
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < C::DBH; ++db) {
-          const u32x2_t g0 = lds_read_tr(gs + 16 * u * D + trd[db][0]);
-          const u32x2_t g1 = lds_read_tr(gs + 16 * u * D + trd[db][1]);
-          const u32x2_t x0 = lds_read_tr(qs + 16 * u * D + trd[db][0]);
-          const u32x2_t x1 = lds_read_tr(qs + 16 * u * D + trd[db][1]);
-          dv[db] = mfma_bf16(u32x4_t{g0[0], g0[1], g1[0], g1[1]}, pk_p[u], dv[db]);
-          dk[db] = mfma_bf16(u32x4_t{x0[0], x0[1], x1[0], x1[1]}, pk_d[u], dk[db]);
-        }
-    };
-
-    issue(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const int st = t & 1;
-      if (t + 1 < ntiles) issue(t + 1, st ^ 1);
-      tile(t, st);
-      wait_vmem();
-      __syncthreads();
-    }
-  }
-
-  // Store this half's columns: lane = key, register r of block db = column
-  // HALF*ch + 32*db + 8*(r/4) + 4*hh + r%4.
-  if (key < a.Tkv) {
-    if (a.kv_split > 1) {
-      const long part = (long)a.B * a.Tkv * krs;
-      float* dkp = a.dkv_part + split * part + kvoff + key * krs + C::HALF * ch;
-      float* dvp = dkp + (long)a.kv_split * part;
-#pragma unroll
-      for (int db = 0; db < C::DBH; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * db + 8 * g + 4 * hh;
-          *(f32x4_t*)(dkp + d) = f32x4_t{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
-          *(f32x4_t*)(dvp + d) = f32x4_t{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
-        }
-    } else {
-      uint16_t* dkp = (uint16_t*)a.dk + kvoff + key * krs + C::HALF * ch;
-      uint16_t* dvp = (uint16_t*)a.dv + kvoff + key * krs + C::HALF * ch;
-#pragma unroll
-      for (int db = 0; db < C::DBH; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = 32 * db + 8 * g + 4 * hh;
-          *(u32x2_t*)(dkp + d) = u32x2_t{pack_bf16(dk[db][4 * g] * a.scale, dk[db][4 * g + 1] * a.scale),
-                                         pack_bf16(dk[db][4 * g + 2] * a.scale, dk[db][4 * g + 3] * a.scale)};
-          *(u32x2_t*)(dvp + d) = u32x2_t{pack_bf16(dv[db][4 * g], dv[db][4 * g + 1]),
-                                         pack_bf16(dv[db][4 * g + 2], dv[db][4 * g + 3])};
-        }
-    }
-  }
-}
 
 // Sum of the kv_split partial dK/dV in split order, rounded to bf16 (dK
 // scaled). Each thread handles 8 consecutive elements of [B, Tkv, Hkv, D].
@@ -1302,7 +1117,7 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kblk0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        pv[r] = (key >= row_lo) & (key <= row_hi) ? pv[r] : 0.f;
+        pv[r] = ((key >= row_lo) & (key <= row_hi)) ? pv[r] : 0.f;
       }
     }
     u32x4_t dsb[2];
@@ -1378,10 +1193,9 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
   } else if (pass == kBwdDkdv) {
     const long kblocks = (long)a.kv_split * a.num_ktiles * a.Hkv * a.B;
     if (kblocks > 0) {
-      if constexpr (D == 256)
-        hipLaunchKernelGGL(attn_dkdv_d256_kernel, dim3((unsigned)(2 * kblocks)), dim3(DkvWideCfg::THREADS), 0, s, a);
-      else if constexpr (D == 128)
-        hipLaunchKernelGGL(attn_dkdv_pair_kernel<D>, dim3((unsigned)kblocks), dim3(DkvPairCfg<D>::THREADS), 0, s, a);
+      if constexpr (D == 128 || D == 256)
+        hipLaunchKernelGGL(attn_dkdv_pair_kernel<D>, dim3((unsigned)(kblocks * (kBwdBlockN / DkvPairCfg<D>::BN))),
+                           dim3(DkvPairCfg<D>::THREADS), 0, s, a);
       else
         hipLaunchKernelGGL(attn_dkdv_bf16_kernel<D>, dim3((unsigned)kblocks), dim3(DkvCfg<D>::THREADS), 0, s, a);
       if (a.kv_split > 1) {

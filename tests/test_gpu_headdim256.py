@@ -2,8 +2,9 @@
 
 The pages report head_dim 256 as a configuration whose tiles overflowed the
 shared memory of the GPU there ("H100 (Hopper)", known issues). Here the
-forward and dQ kernels run one workgroup per compute unit, and dK/dV has its
-own variant that forms one 128-column half of dK and dV per workgroup.
+forward and dQ kernels run one workgroup per compute unit, and dK/dV splits
+each 32-key block over a pair of waves by role (one holds K and dV, the other
+V and dK), two pairs per workgroup, with Q and dO in 32-row tiles.
 """
 
 import pytest
@@ -20,7 +21,7 @@ CASES = [
     Case("d256_T1", 2, 1, 1, 2, 2, 256, workload_id=500),
     Case("d256_T65_causal", 2, 65, 65, 4, 4, 256, causal=True, workload_id=501),
     # B * Hkv * ceil(Tkv/128) = 4 < 256: the query heads of a group split over
-    # workgroups (fp32 partials per column half)
+    # workgroups (fp32 partials of whole rows, summed in split order)
     Case("d256_T200_kvlen_gqa_split", 2, 200, 200, 8, 2, 256, kv_lens=(150, 0), workload_id=502),
     Case("d256_q130_kv300", 2, 130, 300, 4, 4, 256, workload_id=503),
     Case("d256_T333_window_causal", 1, 333, 333, 4, 1, 256, causal=True, window=(70, -1), workload_id=504),
