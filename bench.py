@@ -88,9 +88,9 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel: str):
+def stored_traffic(kernel: str, path: str = ""):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None if stale/missing."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -125,12 +125,12 @@ def _read_counter_csv(directory, counter):
     return out
 
 
-def summarize(stats_dir, fetch_dir, write_dir, command, counter_command):
-    """Write profiles/ summaries from rocprofv3 output (runs on any host)."""
+def summarize(stats_dir, fetch_dir, write_dir, command, counter_command, out_dir=""):
+    """Write profiles/ summaries (or into out_dir) from rocprofv3 output (runs on any host)."""
     import csv
     import glob
 
-    prof = os.path.join(ROOT, "profiles")
+    prof = out_dir or os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     rows = []
     for path in glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True):
@@ -214,7 +214,7 @@ def summarize(stats_dir, fetch_dir, write_dir, command, counter_command):
     print(f"wrote summaries under {prof}")
 
 
-def summarize_fp32(stats_dir, command):
+def summarize_fp32(stats_dir, command, out_dir=""):
     """Per-kernel, per-grid durations of a kernel trace of the fp32 suite (B4 H8, head_dim 64/128)."""
     import csv
     import glob
@@ -262,12 +262,13 @@ def summarize_fp32(stats_dir, command):
             frac = f"{fl / (med * 1e-9) / 1e12 / 157.3:.0%}" if fl else ""
             lines.append(f"| `{name}` | {grid} | {case.name if case else '?'} | {len(part)} | {med / 1e3:.1f} | "
                          f"{tf} | {frac} |")
-    with open(os.path.join(ROOT, "profiles", "fp32_grid_kernel_stats.md"), "w") as f:
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "fp32_grid_kernel_stats.md")
+    with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print("wrote profiles/fp32_grid_kernel_stats.md")
+    print(f"wrote {path}")
 
 
-def summarize_mfma(stats_dir, mfma_dir, command, profile_command):
+def summarize_mfma(stats_dir, mfma_dir, command, profile_command, out_dir=""):
     """MFMA utilisation per kernel at the clock the chip actually ran.
 
     SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD's matrix unit;
@@ -316,7 +317,7 @@ def summarize_mfma(stats_dir, mfma_dir, command, profile_command):
         cyc = g / 8
         lines.append(f"| `{name}` | {n:.4g} | {b / max(n, 1):.1f} | {cyc:.4g} | {dur:.1f} | "
                      f"{cyc / (dur * 1e3):.2f} | {b / (cyc * 1024):.1%} |")
-    with open(os.path.join(ROOT, "profiles", "fwd_bwd_d128_T8192_mfma_util.md"), "w") as f:
+    with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), "fwd_bwd_d128_T8192_mfma_util.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("wrote MFMA utilisation summary")
 

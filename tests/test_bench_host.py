@@ -1,0 +1,109 @@
+"""Host logic of bench.py, on the CPU: the one-GPU contract and the profile
+summaries built from rocprofv3 CSV output (synthetic CSVs, checked against
+numbers worked out by hand)."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+DKDV = "void attn::(anonymous namespace)::attn_dkdv_pair_kernel<128>(attn::BwdArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _counters(path, values):
+    """values: [(kernel, dispatch, grid, counter, value)], one row each."""
+    _write_csv(path, ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"],
+               [[d, g, k, c, v] for k, d, g, c, v in values])
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_summaries_from_synthetic_rocprof_output(tmp_path):
+    stats, fetch, write, mfma, out = (str(tmp_path / n) for n in ("stats", "fetch", "write", "mfma", "out"))
+    os.makedirs(out)
+    _write_csv(os.path.join(stats, "run_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+               [[DKDV, 6, 9300000, 1550000, 100, 1000000, 2100000, 0]])
+    # --warmup 1 --steps 2: the headline leg is 3 dispatches (1 untimed), then the causal leg 3 (1 untimed).
+    durations_us = [2100, 2000, 2000, 1200, 1000, 1000]
+    t = 0
+    rows = []
+    for d in durations_us:
+        rows.append([DKDV, t, t + d * 1000])
+        t += d * 1000 + 500
+    _write_csv(os.path.join(stats, "run_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+               rows)
+    # The copy reads 256 MiB and writes 256 MiB; FETCH_SIZE reads half of it, WRITE_SIZE all of it.
+    _counters(os.path.join(fetch, "run_counter_collection.csv"),
+              [(COPY, 1, 4096, "FETCH_SIZE", 65536.0), (COPY, 1, 4096, "FETCH_SIZE", 65536.0),
+               (DKDV, 2, 524288, "FETCH_SIZE", 200000.0)])
+    _counters(os.path.join(write, "run_counter_collection.csv"),
+              [(COPY, 1, 4096, "WRITE_SIZE", 262144.0), (DKDV, 2, 524288, "WRITE_SIZE", 100000.0)])
+    cyc = 4.2e6  # cycles per XCD during the launch: 2.1 GHz over the 2000 us headline median
+    _counters(os.path.join(mfma, "run_counter_collection.csv"),
+              [(DKDV, d, 524288, c, v) for d in range(1, 7)
+               for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * cyc * 1024), ("SQ_INSTS_MFMA", 7.0e7),
+                            ("GRBM_GUI_ACTIVE", 8 * cyc))])
+    cmd = "rocprofv3 ... -- python3 bench.py --warmup 1 --steps 2"
+    bench.summarize(stats, fetch, write, cmd, "counter command", out_dir=out)
+    bench.summarize_mfma(stats, mfma, "mfma command", cmd, out_dir=out)
+
+    traffic = json.load(open(os.path.join(out, "hbm_traffic.json")))
+    # (200000 KiB x 2 + 100000 KiB x 1) per launch
+    assert traffic["kernels"]["attn_dkdv_pair_kernel"]["bytes_per_launch"] == (200000 * 2 + 100000) * 1024
+    assert traffic["source_digest"] == bench.source_digest()
+    stats_md = open(os.path.join(out, "fwd_bwd_d128_T8192_kernel_stats.md")).read()
+    assert "| `attn_dkdv_pair_kernel<128>` | 3 | 2000.00 | 1000.00 |" in stats_md
+    mfma_md = open(os.path.join(out, "fwd_bwd_d128_T8192_mfma_util.md")).read()
+    assert "| 2000.0 | 2.10 | 50.0% |" in mfma_md
+
+
+def test_stored_traffic_needs_the_current_sources(tmp_path):
+    path = str(tmp_path / "hbm_traffic.json")
+    rec = {"source_digest": bench.source_digest(), "kernels": {"attn_dkdv_pair_kernel": {"bytes_per_launch": 7}}}
+    json.dump(rec, open(path, "w"))
+    assert bench.stored_traffic("attn_dkdv_pair_kernel", path) == 7
+    assert bench.stored_traffic("attn_fwd_bf16_kernel", path) is None
+    rec["source_digest"] = "0" * 16
+    json.dump(rec, open(path, "w"))
+    assert bench.stored_traffic("attn_dkdv_pair_kernel", path) is None
+
+
+@pytest.mark.parametrize("steps", [2])
+def test_fp32_summary_splits_full_and_causal_launches(tmp_path, steps):
+    stats, out = str(tmp_path / "stats"), str(tmp_path / "out")
+    os.makedirs(out)
+    name = "void attn::(anonymous namespace)::attn_fwd_f32_kernel<128>(attn::FwdArgs)"
+    grid = 256 * (4096 // 128) * 8 * 4  # B4 H8 T4096, 128 query rows per workgroup
+    rows, t = [], 0
+    for d in (2200, 2200, 2210, 1250, 1240, 1250):  # non-causal launches first, then causal
+        rows.append([name, t, t + d * 1000, grid])
+        t += d * 1000 + 500
+    _write_csv(os.path.join(stats, "run_kernel_trace.csv"),
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"], rows)
+    bench.summarize_fp32(stats, "cmd", out_dir=out)
+    md = open(os.path.join(out, "fp32_grid_kernel_stats.md")).read()
+    # 4 B H T^2 D = 2.749e11 flop in 2.2 ms; half of it in 1.25 ms when causal.
+    assert "| fp32_d128_T4096_full | 3 | 2200.0 | 124.9 | 79% |" in md
+    assert "| fp32_d128_T4096_causal | 3 | 1250.0 | 110.0 | 70% |" in md
