@@ -2,7 +2,8 @@
 
 The pages report head_dim 256 as a configuration whose tiles overflowed the
 shared memory of the GPU there ("H100 (Hopper)", known issues). Here the
-forward and dQ kernels run one workgroup per compute unit, and dK/dV splits
+forward splits each query block over a pair of waves by role (S and softmax;
+O), dQ runs one workgroup per compute unit, and dK/dV splits
 each 32-key block over a pair of waves by role (one holds K and dV, the other
 V and dK), two pairs per workgroup, with Q and dO in 32-row tiles.
 """
