@@ -178,7 +178,6 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
   a.win_left = window_bound(p->window_left, p->Tkv); a.win_right = window_bound(p->window_right, p->Tkv);
-  a.num_qtiles = (p->Tq + attn::kBwdBlockM - 1) / attn::kBwdBlockM;
   a.num_ktiles = (p->Tkv + attn::kBwdBlockN - 1) / attn::kBwdBlockN;
   return ATTN_OK;
 }

@@ -727,10 +727,14 @@ __global__ __launch_bounds__(256) void attn_dkdv_reduce_kernel(BwdArgs a, long n
 }
 
 // --------------------------------------------------------------------- dQ
+//
+// Single-pair dQ kernel (head_dim 32 and 256; 64 and 128 run the wave-pair
+// kernel further below): four waves of 32 query rows, each processing both
+// 32-key blocks of every 64-key tile.
 
 template <int D>
 struct DqCfg {
-  static constexpr int BM = 128;            // query rows, 32 per wave
+  static constexpr int BM = kBwdBlockM;     // 128 query rows, 32 per wave
   static constexpr int BN = 64;             // keys per tile (2 blocks of 32)
   static constexpr int THREADS = 256;
   static constexpr int KS = D / 16;
@@ -998,7 +1002,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
 // dP^T = V dO^T (lane = query row), dS^T = P (dP - D), dQ^T += K^T dS^T.
 template <int D>
 struct DqPairCfg {
-  static constexpr int BM = 128;            // query rows, 32 per wave pair
+  static constexpr int BM = kBwdBlockM;     // 128 query rows, 32 per wave pair
   static constexpr int BN = 64;             // keys per tile (one 32-key block per wave of a pair)
   static constexpr int THREADS = 512;
   static constexpr int KS = D / 16;
@@ -1204,7 +1208,7 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
       }
     }
   } else {
-    const long nqt = (a.Tq + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+    const long nqt = (a.Tq + kBwdBlockM - 1) / kBwdBlockM;
     const long qblocks = nqt * a.Hq * a.B;
     if (qblocks > 0) {
       if constexpr (D == 64 || D == 128)

@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdAr
 
 template <int D>
 struct F32DqCfg {
-  static constexpr int BM = 128;              // query rows, 32 per wave
+  static constexpr int BM = kBwdBlockM;       // 128 query rows, 32 per wave
   static constexpr int BN = 64;               // keys per tile (two 32-key blocks)
   static constexpr int THREADS = 256;
   static constexpr int KG = D / 8;
@@ -961,7 +961,7 @@ hipError_t launch_bwd_pass_fp32(const BwdArgs& a, int D, int pass, hipStream_t s
         hipLaunchKernelGGL(attn_dkdv_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     }
   } else {
-    const long blocks = (long)((a.Tq + F32DqCfg<64>::BM - 1) / F32DqCfg<64>::BM) * a.Hq * a.B;
+    const long blocks = (long)((a.Tq + kBwdBlockM - 1) / kBwdBlockM) * a.Hq * a.B;
     if (blocks > 0) {
       if (D == 128)
         hipLaunchKernelGGL(attn_dq_f32_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);

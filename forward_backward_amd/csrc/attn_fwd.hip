@@ -47,10 +47,10 @@ struct FwdCfg {
   static constexpr int TILE = BN * D;         // elements of one K or V tile
 };
 
-// Two workgroups per compute unit up to head_dim 128; at 256 the output
-// accumulators alone take 128 registers per lane and the K/V rings 128 KiB.
+// Two workgroups per compute unit (head_dim 32, 64 and 128; head_dim 256 runs
+// the wave-pair kernel below).
 template <int D>
-__global__ __launch_bounds__(256, D > 128 ? 1 : 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_s0[C::TILE], k_s1[C::TILE], v_s0[C::TILE], v_s1[C::TILE];
 

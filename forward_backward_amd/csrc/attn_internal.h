@@ -44,7 +44,6 @@ struct BwdArgs {
   float scale_log2;
   int causal;
   int win_left, win_right; // local window bounds, -1 = none (see key_lo / key_hi)
-  int num_qtiles;          // query tiles of the dQ kernel
   int num_ktiles;          // KV tiles of the dK/dV kernel
   int kv_split;            // dK/dV workgroups per KV tile, each over heads_per_split query heads of the group
   int heads_per_split;
@@ -80,7 +79,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s);
 
 // Tile sizes the host needs for grids and workspaces.
 constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
-constexpr int kBwdBlockM = 64;    // query rows per dQ workgroup
+constexpr int kBwdBlockM = 128;   // query rows per dQ workgroup
 constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
 constexpr int kBwdFillTarget = 256;  // dK/dV workgroups below which a group's query heads are split (one per CU)
 constexpr int kDecodeTileN = 64;  // keys per decode iteration
