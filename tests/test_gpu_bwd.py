@@ -89,3 +89,39 @@ def test_bwd_kv_length_workload_sampled():
     # Batch 0 has a single valid key: the exact dQ and dK are zero.
     assert float(to_host64(dq[0]).__abs__().max()) <= 1e-3
     assert float(to_host64(dk[0]).__abs__().max()) <= 1e-3
+
+
+@pytest.mark.parametrize("case", [
+    # B * Hkv * ceil(Tkv / 128) = 6 < 256: dK/dV splits the group's query heads
+    # and writes fp32 partials into the workspace that dQ reads from too.
+    Case("streams_d128_gqa_split_causal_kvlen", 1, 300, 300, 8, 2, 128, causal=True, kv_lens=(250,),
+         workload_id=121),
+    Case("streams_d64_window", 2, 500, 500, 4, 4, 64, window=(60, 10), workload_id=122),
+], ids=lambda c: c.name)
+def test_dkdv_and_dq_on_two_streams_match_the_sequential_call(case):
+    """The dK/dV and dQ passes only read what the pre-pass wrote, so a caller
+    may run them concurrently on two streams; the result must be the
+    sequential call's, bit for bit."""
+    import torch
+    from forward_backward_amd import attn
+    host, dev, _ = device_inputs(case)
+    print(f"[bwd two streams] {case.name}", flush=True)
+    kw = dict(scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"], window=case.window)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = attn.fwd(q, k, v, **kw)
+    dq_ref, dk_ref, dv_ref = attn.bwd(q, k, v, o, lse, do, **kw)
+    ws = attn.bwd_workspace(q, k, causal=case.causal, kv_lens=dev["kv_lens"], window=case.window)
+    attn.bwd_preprocess(o, lse, do, ws, q, k, **kw)
+    ready = torch.cuda.Event()
+    ready.record()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        s1.wait_event(ready)
+        attn.bwd_dkdv(q, k, v, lse, do, ws, dk, dv, **kw)
+    with torch.cuda.stream(s2):
+        s2.wait_event(ready)
+        attn.bwd_dq(q, k, v, lse, do, ws, dq, **kw)
+    torch.cuda.synchronize()
+    for got, ref in ((dq, dq_ref), (dk, dk_ref), (dv, dv_ref)):
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
