@@ -125,3 +125,17 @@ def test_dkdv_and_dq_on_two_streams_match_the_sequential_call(case):
     torch.cuda.synchronize()
     for got, ref in ((dq, dq_ref), (dk, dk_ref), (dv, dv_ref)):
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", [
+    # 32 query heads on one KV head: the dK/dV head split runs 32 ways
+    # (B * Hkv * ceil(Tkv / 128) = 2 workgroups without it) and the
+    # reduction sums 32 fp32 partials per element.
+    Case("gqa32_split32_d128_T200", 1, 200, 200, 32, 1, 128, workload_id=123),
+    Case("gqa16_d64_T333_causal_kvlen", 2, 333, 333, 16, 1, 64, causal=True, kv_lens=(333, 129), workload_id=124),
+    Case("gqa16_d256_T130_kvlen", 1, 130, 130, 16, 1, 256, kv_lens=(77,), workload_id=125),
+    # Many short problems: 16 sequences of 64 tokens.
+    Case("b16_d128_T64", 16, 64, 64, 4, 2, 128, workload_id=126),
+], ids=lambda c: c.name)
+def test_bwd_wide_groups_and_many_short_sequences(case):
+    check_bwd(case)
