@@ -157,7 +157,10 @@ constexpr float kRescaleLog2F32 = 8.f;  // rescale O only when a row max grows b
 template <int D>
 struct F32FwdCfg {
   static constexpr int BM = kFwdBlockM;       // 128 query rows, 32 per wave
-  static constexpr int BN = 64;               // keys per tile (two 32-key blocks)
+  // Keys per tile: two 32-key blocks up to head_dim 64; one at 128, so that
+  // the K/V rings take 64 KiB and two workgroups share a compute unit.
+  static constexpr int NX = D > 64 ? 1 : 2;
+  static constexpr int BN = 32 * NX;
   static constexpr int THREADS = 256;
   static constexpr int KG = D / 8;            // 16-byte reads per lane over head_dim
   static constexpr int NB = D / 32;           // output blocks over head_dim
@@ -165,14 +168,14 @@ struct F32FwdCfg {
   static constexpr int TILE = BN * D;
 };
 
-// One workgroup = 4 waves = 128 query rows of one (batch, head). Per 64-key
-// tile: S^T = K Q^T (lane = query row, Q in registers as the B operand), the
+// One workgroup = 4 waves = 128 query rows of one (batch, head). Per key
+// tile (64 keys, 32 at head_dim 128): S^T = K Q^T (lane = query row, Q in registers as the B operand), the
 // online softmax in base 2 with lazy rescaling (as the bf16 forward), then
 // O^T += V^T P^T with P straight from the S accumulators. K and V stream
 // through two-stage LDS rings, K one tile ahead; the next tile's S^T is
 // issued before the current tile's softmax so the two overlap.
 template <int D>
-__global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_f32_kernel(FwdArgs a) {
   using C = F32FwdCfg<D>;
   // K stages 0 and 1, then V stages 0 and 1. Stages are picked at run time:
   // with constant stage addresses the compiler keeps a copy of every lane
@@ -249,41 +252,58 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdAr
   const int wave_all_lo = key_lo(wave_min_row + 31, a.win_left);
   const int wave_all_hi = key_hi(wave_min_row, kvlim, a.causal, a.win_right);
 
-  int nrm[C::KG], vrd[16];
+  // Lane offsets. Head_dim groups g and g + 8 (head_dim 128) lie 64 elements
+  // apart under the same swizzle, and so do rows t and t + 8 of a block
+  // (16 rows), so eight of each are kept.
+  constexpr int NG = C::KG < 8 ? C::KG : 8;
+  int nrm8[NG], vrd8[8];
 #pragma unroll
-  for (int g = 0; g < C::KG; ++g) nrm[g] = swz4_off<D>(l32, 8 * g + 4 * hh);
+  for (int g = 0; g < NG; ++g) nrm8[g] = swz4_off<D>(l32, 8 * g + 4 * hh);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) vrd[t] = swz4_off<D>(8 * (t >> 2) + 4 * hh + (t & 3), C::NB * l32);
+  for (int t = 0; t < 8; ++t) vrd8[t] = swz4_off<D>(8 * (t >> 2) + 4 * hh + (t & 3), C::NB * l32);
+  auto nrm = [&](int g) { return nrm8[g & 7] + (g >> 3) * 64; };
+  auto vrd = [&](int t) { return vrd8[t & 7] + (t >> 3) * 16 * D; };
 
-  auto sdot = [&](const float* kl, f32x16_t (&s)[2]) {
-    s[0] = f32x16_t{};
-    s[1] = f32x16_t{};
-    f32x4_t n0 = *(const f32x4_t*)(kl + nrm[0]);
-    f32x4_t n1 = *(const f32x4_t*)(kl + 32 * D + nrm[0]);
+  // S^T of the tile's key blocks (with one block the products form one chain;
+  // the second workgroup on the SIMD fills its gaps).
+  auto sdot = [&](const float* kl, f32x16_t (&s)[C::NX]) {
+    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+    f32x4_t n0 = *(const f32x4_t*)(kl + nrm(0));
+    f32x4_t n1 = *(const f32x4_t*)(kl + (C::NX - 1) * 32 * D + nrm(0));
 #pragma unroll
     for (int g = 0; g < C::KG; ++g) {
       const f32x4_t k0v = n0, k1v = n1;
       if (g + 1 < C::KG) {
-        n0 = *(const f32x4_t*)(kl + nrm[g + 1]);
-        n1 = *(const f32x4_t*)(kl + 32 * D + nrm[g + 1]);
+        n0 = *(const f32x4_t*)(kl + nrm(g + 1));
+        if constexpr (C::NX == 2) n1 = *(const f32x4_t*)(kl + 32 * D + nrm(g + 1));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        s[0] = mfma_f32(k0v[j], qf[4 * g + j], s[0]);
-        s[1] = mfma_f32(k1v[j], qf[4 * g + j], s[1]);
+        if constexpr (C::NX == 2) {
+          acc[0] = mfma_f32(k0v[j], qf[4 * g + j], acc[0]);
+          acc[1] = mfma_f32(k1v[j], qf[4 * g + j], acc[1]);
+        } else {
+          acc[0] = mfma_f32(k0v[j], qf[4 * g + j], acc[0]);
+        }
       }
       fence();
+    }
+    if constexpr (C::NX == 2) {
+      s[0] = acc[0];
+      s[C::NX - 1] = acc[1];
+    } else {
+      s[0] = acc[0];
     }
   };
 
   // S -> P (unnormalised) in place; returns whether O must be rescaled by
   // alpha (wave-uniform).
-  auto softmax = [&](auto mask_tag, int j, f32x16_t (&s)[2], float& alpha) -> bool {
+  auto softmax = [&](auto mask_tag, int j, f32x16_t (&s)[C::NX], float& alpha) -> bool {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = (j0 + j) * C::BN;
     if constexpr (MASK) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < C::NX; ++x)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * x + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -293,7 +313,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdAr
     }
     float mt = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < C::NX; ++x)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[x][r]);
     mt = half_max(mt);
@@ -306,7 +326,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdAr
     const float nb = (m == -INFINITY) ? 0.f : -m * c;
     float ps = 0.f;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < C::NX; ++x)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(__builtin_fmaf(s[x][r], c, nb));
@@ -317,23 +337,23 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdAr
     return any;
   };
 
-  auto pv = [&](const float* vl, const f32x16_t (&s)[2]) {
-    float n[2][C::NB];
-    lds_vec<C::NB>(vl + vrd[0], n[0]);
-    lds_vec<C::NB>(vl + 32 * D + vrd[0], n[1]);
+  auto pv = [&](const float* vl, const f32x16_t (&s)[C::NX]) {
+    float n[C::NX][C::NB];
+#pragma unroll
+    for (int x = 0; x < C::NX; ++x) lds_vec<C::NB>(vl + 32 * x * D + vrd(0), n[x]);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      float vv[2][C::NB];
+      float vv[C::NX][C::NB];
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < C::NX; ++x)
 #pragma unroll
         for (int e = 0; e < C::NB; ++e) vv[x][e] = n[x][e];
       if (t + 1 < 16) {
-        lds_vec<C::NB>(vl + vrd[t + 1], n[0]);
-        lds_vec<C::NB>(vl + 32 * D + vrd[t + 1], n[1]);
+#pragma unroll
+        for (int x = 0; x < C::NX; ++x) lds_vec<C::NB>(vl + 32 * x * D + vrd(t + 1), n[x]);
       }
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
+      for (int x = 0; x < C::NX; ++x) {
         if constexpr (C::NB > 1) {
 #pragma unroll
           for (int db = 0; db < C::NB; ++db) o[db] = mfma_f32(vv[x][db], s[x][t], o[db]);
@@ -345,7 +365,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdAr
     }
   };
 
-  f32x16_t s_cur[2], s_nxt[2];
+  f32x16_t s_cur[C::NX], s_nxt[C::NX];
   if (ntiles > 0) {
     wait_vmem();
     __syncthreads();
@@ -379,8 +399,8 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_fwd_f32_kernel(FwdAr
       for (int i = 0; i < C::NO; ++i) o[i] *= alpha;
     }
     pv(vc, s_cur);
-    s_cur[0] = s_nxt[0];
-    s_cur[1] = s_nxt[1];
+#pragma unroll
+    for (int x = 0; x < C::NX; ++x) s_cur[x] = s_nxt[x];
     wait_vmem();
     __syncthreads();
   };
