@@ -435,7 +435,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_f32_kernel(FwdArgs a) {
 template <int D>
 struct F32DqCfg {
   static constexpr int BM = kBwdBlockM;       // 128 query rows, 32 per wave
-  static constexpr int BN = 64;               // keys per tile (two 32-key blocks)
+  static constexpr int NX = 2;                // 32-key blocks per tile
+  static constexpr int BN = 32 * NX;
   static constexpr int THREADS = 256;
   static constexpr int KG = D / 8;
   static constexpr int NB = D / 32;
@@ -449,8 +450,10 @@ struct F32DqCfg {
 // accumulators. Both blocks' products are issued before the first softmax so
 // that the vector work overlaps the matrix core. K and V tiles stream through
 // a two-stage LDS ring.
+// Two workgroups per compute unit up to head_dim 64; at 128 Q, dO and dQ^T
+// alone take 192 registers per lane.
 template <int D>
-__global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dq_f32_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_dq_f32_kernel(BwdArgs a) {
   using C = F32DqCfg<D>;
   // Stage s holds K at tiles + 2s TILE and V after it; stages are picked at
   // run time (see the forward).
@@ -528,25 +531,29 @@ __global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dq_f32_kernel(BwdArg
   const int row_hi = key_hi(qrow, kvlim, a.causal, a.win_right);
   const int wave_all_lo = key_lo(wave_min_row + 31, a.win_left);
   const int wave_all_hi = key_hi(wave_min_row, kvlim, a.causal, a.win_right);
-  int nrm[C::KG], vrd[16];
+  // Lane offsets, eight of each (see the forward).
+  constexpr int NG = C::KG < 8 ? C::KG : 8;
+  int nrm8[NG], vrd8[8];
 #pragma unroll
-  for (int g = 0; g < C::KG; ++g) nrm[g] = swz4_off<D>(l32, 8 * g + 4 * hh);
+  for (int g = 0; g < NG; ++g) nrm8[g] = swz4_off<D>(l32, 8 * g + 4 * hh);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) vrd[t] = swz4_off<D>(8 * (t >> 2) + 4 * hh + (t & 3), C::NB * l32);
+  for (int t = 0; t < 8; ++t) vrd8[t] = swz4_off<D>(8 * (t >> 2) + 4 * hh + (t & 3), C::NB * l32);
+  auto nrm = [&](int g) { return nrm8[g & 7] + (g >> 3) * 64; };
+  auto vrd = [&](int t) { return vrd8[t & 7] + (t >> 3) * 16 * D; };
 
   auto sdp = [&](const float* kl, const float* vl, int x, f32x16_t& s, f32x16_t& dp) {
     s = f32x16_t{};
     dp = f32x16_t{};
     const float* kx = kl + 32 * x * D;
     const float* vx = vl + 32 * x * D;
-    f32x4_t nk = *(const f32x4_t*)(kx + nrm[0]);
-    f32x4_t nv = *(const f32x4_t*)(vx + nrm[0]);
+    f32x4_t nk = *(const f32x4_t*)(kx + nrm(0));
+    f32x4_t nv = *(const f32x4_t*)(vx + nrm(0));
 #pragma unroll
     for (int g = 0; g < C::KG; ++g) {
       const f32x4_t kv = nk, vv = nv;
       if (g + 1 < C::KG) {
-        nk = *(const f32x4_t*)(kx + nrm[g + 1]);
-        nv = *(const f32x4_t*)(vx + nrm[g + 1]);
+        nk = *(const f32x4_t*)(kx + nrm(g + 1));
+        nv = *(const f32x4_t*)(vx + nrm(g + 1));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -573,13 +580,13 @@ __global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dq_f32_kernel(BwdArg
   auto dq = [&](const float* kl, int x, const f32x16_t& ds) {
     const float* kx = kl + 32 * x * D;
     float n[C::NB];
-    lds_vec<C::NB>(kx + vrd[0], n);
+    lds_vec<C::NB>(kx + vrd(0), n);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       float kv[C::NB];
 #pragma unroll
       for (int e = 0; e < C::NB; ++e) kv[e] = n[e];
-      if (t + 1 < 16) lds_vec<C::NB>(kx + vrd[t + 1], n);
+      if (t + 1 < 16) lds_vec<C::NB>(kx + vrd(t + 1), n);
       if constexpr (C::NB > 1) {
 #pragma unroll
         for (int db = 0; db < C::NB; ++db) acc[db] = mfma_f32(kv[db], ds[t], acc[db]);
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dq_f32_kernel(BwdArg
     const int k0 = (j0 + it) * C::BN;
     const bool mask_tile = (k0 < wave_all_lo) || (k0 + C::BN - 1 > wave_all_hi);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
+    for (int x = 0; x < C::NX; ++x) {
       f32x16_t s, dp;
       sdp(kl, vl, x, s, dp);
       if (mask_tile)
@@ -654,7 +661,7 @@ struct F32DkvCfg {
 // dK^T += Q^T dS with P and dS straight from the accumulators. Q, dO and the
 // rows' LSE log2 e and D stream through a two-stage LDS ring.
 template <int D>
-__global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dkdv_f32_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_dkdv_f32_kernel(BwdArgs a) {
   using C = F32DkvCfg<D>;
   constexpr int STAGE = 2 * C::TILE + 2 * C::BM;  // Q, dO, LSE log2 e, D (floats)
   __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
@@ -735,25 +742,29 @@ __global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dkdv_f32_kernel(BwdA
     for (int i = 0; i < D / 2; ++i) asm volatile("" ::"v"(kf[i]), "v"(vf[i]));
 
     const float c = a.scale_log2;
-    int nrm[C::KG], vrd[16];
+    // Lane offsets, eight of each (see the forward).
+    constexpr int NG = C::KG < 8 ? C::KG : 8;
+    int nrm8[NG], vrd8[8];
 #pragma unroll
-    for (int g = 0; g < C::KG; ++g) nrm[g] = swz4_off<D>(l32, 8 * g + 4 * hh);
+    for (int g = 0; g < NG; ++g) nrm8[g] = swz4_off<D>(l32, 8 * g + 4 * hh);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) vrd[t] = swz4_off<D>(8 * (t >> 2) + 4 * hh + (t & 3), C::NB * l32);
+    for (int t = 0; t < 8; ++t) vrd8[t] = swz4_off<D>(8 * (t >> 2) + 4 * hh + (t & 3), C::NB * l32);
+    auto nrm = [&](int g) { return nrm8[g & 7] + (g >> 3) * 64; };
+    auto vrd = [&](int t) { return vrd8[t & 7] + (t >> 3) * 16 * D; };
 
     auto sp = [&](const float* ql, const float* gl, int x, f32x16_t& s, f32x16_t& dp) {
       s = f32x16_t{};
       dp = f32x16_t{};
       const float* qx = ql + 32 * x * D;
       const float* gx = gl + 32 * x * D;
-      f32x4_t nq = *(const f32x4_t*)(qx + nrm[0]);
-      f32x4_t ng = *(const f32x4_t*)(gx + nrm[0]);
+      f32x4_t nq = *(const f32x4_t*)(qx + nrm(0));
+      f32x4_t ng = *(const f32x4_t*)(gx + nrm(0));
 #pragma unroll
       for (int g = 0; g < C::KG; ++g) {
         const f32x4_t qv = nq, gv = ng;
         if (g + 1 < C::KG) {
-          nq = *(const f32x4_t*)(qx + nrm[g + 1]);
-          ng = *(const f32x4_t*)(gx + nrm[g + 1]);
+          nq = *(const f32x4_t*)(qx + nrm(g + 1));
+          ng = *(const f32x4_t*)(gx + nrm(g + 1));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -789,8 +800,8 @@ __global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dkdv_f32_kernel(BwdA
       const float* qx = ql + 32 * x * D;
       const float* gx = gl + 32 * x * D;
       float ng[C::NB], nq[C::NB];
-      lds_vec<C::NB>(gx + vrd[0], ng);
-      lds_vec<C::NB>(qx + vrd[0], nq);
+      lds_vec<C::NB>(gx + vrd(0), ng);
+      lds_vec<C::NB>(qx + vrd(0), nq);
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         float gv[C::NB], qv[C::NB];
@@ -800,8 +811,8 @@ __global__ __launch_bounds__(256, D > 32 ? 1 : 2) void attn_dkdv_f32_kernel(BwdA
           qv[e] = nq[e];
         }
         if (t + 1 < 16) {
-          lds_vec<C::NB>(gx + vrd[t + 1], ng);
-          lds_vec<C::NB>(qx + vrd[t + 1], nq);
+          lds_vec<C::NB>(gx + vrd(t + 1), ng);
+          lds_vec<C::NB>(qx + vrd(t + 1), nq);
         }
         if constexpr (C::NB > 1) {
 #pragma unroll
