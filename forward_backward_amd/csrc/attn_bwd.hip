@@ -82,8 +82,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
   const int hh = lane >> 5;
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = bid % a.num_ktiles;
-  int rest = bid / a.num_ktiles;
+  int kt, rest;  // rank 0: the first key tile, the most query rows when causal
+  tile_order(bid, a.num_ktiles, a.kv_split * a.B * a.Hkv, a.causal, rest, kt);
   const int kh = rest % a.Hkv;
   rest /= a.Hkv;
   const int b = rest % a.B;
@@ -439,8 +439,8 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int nkt = a.num_ktiles * (kBwdBlockN / C::BN);  // workgroups per (batch, KV head, split)
-  const int kt = bid % nkt;
-  int rest = bid / nkt;
+  int kt, rest;  // rank 0: the first key tile, the most query rows when causal
+  tile_order(bid, nkt, a.kv_split * a.B * a.Hkv, a.causal, rest, kt);
   const int kh = rest % a.Hkv;
   rest /= a.Hkv;
   const int b = rest % a.B;
@@ -761,8 +761,9 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
 
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = nqt - 1 - (bid % nqt);
-  const int bh = bid / nqt;
+  int bh, rank;
+  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank);
+  const int qt = nqt - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kh = h / (a.Hq / a.Hkv);
@@ -1027,8 +1028,9 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
 
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = nqt - 1 - (bid % nqt);
-  const int bh = bid / nqt;
+  int bh, rank;
+  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank);
+  const int qt = nqt - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kh = h / (a.Hq / a.Hkv);

@@ -263,6 +263,32 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return start + bid / kXcds;
 }
 
+// Order of a grid's tiles over the remapped workgroup ids: `nunits` units
+// (a batch and head, say) of `ntiles` tiles each; returns the unit and the
+// tile rank t (t = 0 is the unit's most expensive tile). Without causal
+// masking every tile costs the same, and a unit's tiles stay adjacent so that
+// the XCD running them shares the unit's K/V rows in its L2. With causal
+// masking the costs fall linearly with t; issued unit by unit, a tile count
+// per unit unequal to the number of workgroups resident on an XCD leaves long
+// tiles for last (up to 1.5 times the balanced time in a list-scheduling
+// model). So the units are cut into groups, one per XCD when their number is
+// a multiple of 8, and each group issues its tiles rank by rank (longest
+// first) across its units.
+__device__ __forceinline__ void tile_order(int bid, int ntiles, int nunits, bool longest_first, int& unit,
+                                           int& t) {
+  if (!longest_first) {
+    unit = bid / ntiles;
+    t = bid % ntiles;
+    return;
+  }
+  const int gsz = nunits >= 8 ? nunits / 8 : 1;     // units per group
+  const int g = bid / (gsz * ntiles);
+  const int gs = min(gsz, nunits - g * gsz);        // units in this group (the last may be short)
+  const int p = bid - g * gsz * ntiles;
+  t = p / gs;
+  unit = g * gsz + p % gs;
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int tkv) {
   if (kv_lens == nullptr) return tkv;
   int n = kv_lens[b];

@@ -191,8 +191,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_f32_kernel(FwdArgs a) {
   const int hh = lane >> 5;
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = a.num_qtiles - 1 - (bid % a.num_qtiles);  // longest causal tiles first
-  const int bh = bid / a.num_qtiles;
+  int bh, rank;
+  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank);
+  const int qt = a.num_qtiles - 1 - rank;  // rank 0: the last query tile, the most keys when causal
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kh = h / (a.Hq / a.Hkv);
@@ -467,8 +468,9 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_dq_f32_kernel(BwdArg
 
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = nqt - 1 - (bid % nqt);
-  const int bh = bid / nqt;
+  int bh, rank;
+  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank);
+  const int qt = nqt - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kh = h / (a.Hq / a.Hkv);
@@ -673,9 +675,10 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_dkdv_f32_kernel(BwdA
   const int hh = lane >> 5;
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = bid % a.num_ktiles;
-  const int kh = (bid / a.num_ktiles) % a.Hkv;
-  const int b = bid / (a.num_ktiles * a.Hkv);
+  int kt, unit;  // rank 0: the first key tile, the most query rows when causal
+  tile_order(bid, a.num_ktiles, a.B * a.Hkv, a.causal, unit, kt);
+  const int kh = unit % a.Hkv;
+  const int b = unit / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int k0 = kt * C::BN;
   const int wk0 = k0 + 32 * wave;

@@ -61,8 +61,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int hh = lane >> 5;
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = a.num_qtiles - 1 - (bid % a.num_qtiles);  // longest causal tiles first
-  const int bh = bid / a.num_qtiles;
+  int bh, rank;
+  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank);
+  const int qt = a.num_qtiles - 1 - rank;  // rank 0: the last query tile, the most keys when causal
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kh = h / (a.Hq / a.Hkv);
@@ -339,8 +340,9 @@ __global__ __launch_bounds__(FwdPairCfg<D>::THREADS) void attn_fwd_pair_kernel(F
   const int hh = lane >> 5;
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = a.num_qtiles - 1 - (bid % a.num_qtiles);
-  const int bh = bid / a.num_qtiles;
+  int bh, rank;
+  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank);
+  const int qt = a.num_qtiles - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kh = h / (a.Hq / a.Hkv);
