@@ -1009,14 +1009,15 @@ struct DqPairCfg {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int R = 2;               // depth of the fragment read-ahead
+  static constexpr int NST = 3;             // K/V stages: tiles are copied two ahead
   static constexpr int TILE = BN * D;
 };
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
   using C = DqPairCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * C::TILE];  // stage s: K at 2s, V at 2s + 1
-  static_assert(4 * C::TILE * 2 >= 4 * 64 * 16 * C::DB * 4, "the partial hand-over reuses the tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2 * C::NST * C::TILE];  // stage s: K at 2s, V at 2s + 1
+  static_assert(2 * C::NST * C::TILE * 2 >= 4 * 64 * 16 * C::DB * 4, "the partial hand-over reuses the tiles");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1082,11 +1083,21 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col) + 32 * half * D;
   }
 
-  auto issue = [&](int it) {
-    uint16_t* ks = tiles + (it & 1) * 2 * C::TILE;
+  // Copies of tile `it` into stage `st`. They go through inline assembly, which
+  // the compiler does not see writing LDS: the waits before each tile's barrier
+  // order them (CP copy instructions per wave and tile, full or partial).
+  const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
+  constexpr int CP = 2 * TileCopy<D, C::BN, C::THREADS>::ITERS;
+  auto issue = [&](int it, int st) {
+    uint16_t* ks = tiles + st * 2 * C::TILE;
     const int k0 = (j0 + it) * C::BN;
-    dma_tile<D, C::BN, C::THREADS, true>(ks, kb, krs, k0, kv_end, tid);
-    dma_tile<D, C::BN, C::THREADS, true>(ks + C::TILE, vb, krs, k0, kv_end, tid);
+    if (k0 + C::BN <= kv_end) {
+      kvcopy.copy(ks, kb, krs, k0);
+      kvcopy.copy(ks + C::TILE, vb, krs, k0);
+    } else {
+      dma_tile<D, C::BN, C::THREADS>(ks, kb, krs, k0, kv_end, tid);
+      dma_tile<D, C::BN, C::THREADS>(ks + C::TILE, vb, krs, k0, kv_end, tid);
+    }
   };
 
   // One 32-key block: S^T, dP^T, the masked dS^T, then dQ^T += K^T dS^T. The
@@ -1151,16 +1162,28 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     }
   };
 
-  if (ntiles > 0) issue(0);
+  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+  // The Q and dO fragments and the first tiles have landed: without this the
+  // compiler, which only sees the fragment loads, waits for them inside the
+  // loop, where the wait would also drain the copies in flight.
+  wait_vmem();
+  int st_rd = 0, st_wr = 2;
   for (int it = 0; it < ntiles; ++it) {
-    wait_vmem();
-    __syncthreads();  // tile it landed; every wave is done with tile it - 1
-    if (it + 1 < ntiles) issue(it + 1);
-    const uint16_t* kl = tiles + (it & 1) * 2 * C::TILE;
+    // Tile it has landed once at most the copies of tile it + 1 are in flight.
+    if (it + 1 < ntiles)
+      wait_vmcnt<CP>();
+    else
+      wait_vmem();
+    __syncthreads();  // tile it visible; every wave is done with tile it - 1, whose stage is refilled next
+    if (it + 2 < ntiles) issue(it + 2, st_wr);
+    const uint16_t* kl = tiles + st_rd * 2 * C::TILE;
     const int k0 = (j0 + it) * C::BN;
     const int kblk0 = k0 + 32 * half;
     const bool mask = (kblk0 < wave_all_lo) || (kblk0 + 31 > wave_all_hi);
     block(mask, kl, kl + C::TILE, kblk0);
+    st_rd = st_rd + 1 == C::NST ? 0 : st_rd + 1;
+    st_wr = st_wr + 1 == C::NST ? 0 : st_wr + 1;
   }
 
   // The pair's partials: block-1 waves hand theirs over through LDS, block-0
