@@ -74,6 +74,10 @@ def parse_args():
     ap.add_argument("--mfma-dir", default="", help="with --summarize: rocprofv3 output of a pass with "
                     "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
     ap.add_argument("--mfma-command", default="", help="MFMA counter-pass command recorded in the summaries")
+    ap.add_argument("--summarize-stalls", nargs="+", metavar="PMC_DIR",
+                    help="turn rocprofv3 --pmc passes over the headline run (issue, wait, co-issue and LDS counters) "
+                         "into profiles/fwd_bwd_d128_T8192_issue_counters.md and exit (no GPU use); "
+                         "--counter-command records the command of each pass")
     return ap.parse_args()
 
 
@@ -679,8 +683,83 @@ def cpu_baseline(case, seconds):
     }
 
 
+STALL_COUNTERS = {
+    "SQ_WAVE_CYCLES": "wave-cycles (quad-cycles) the kernel's waves were resident",
+    "SQ_ACTIVE_INST_ANY": "wave-cycles an instruction of the wave was being executed",
+    "SQ_WAIT_ANY": "wave-cycles spent waiting on anything (s_waitcnt, barrier, dependency)",
+    "SQ_WAIT_INST_ANY": "wave-cycles spent waiting for an issue slot",
+    "SQ_WAIT_INST_LDS": "wave-cycles spent waiting to issue an LDS instruction",
+    "SQ_ACTIVE_INST_VALU": "wave-cycles on VALU instructions",
+    "SQ_ACTIVE_INST_LDS": "wave-cycles on LDS instructions",
+    "SQ_VALU_MFMA_BUSY_CYCLES": "cycles the matrix units were busy (all SIMDs)",
+    "SQ_VALU_MFMA_COEXEC_CYCLES": "of those, cycles in which a VALU instruction was issued too",
+    "SQ_INSTS_MFMA": "MFMA instructions",
+    "SQ_INSTS_VALU": "VALU instructions",
+    "SQ_INSTS_SALU": "SALU instructions",
+    "SQ_INSTS_LDS": "LDS instructions",
+    "SQ_LDS_BANK_CONFLICT": "LDS bank-conflict cycles",
+    "SQ_LDS_IDX_ACTIVE": "LDS busy cycles",
+}
+
+
+def summarize_stalls(pmc_dirs, command, out_dir=""):
+    """Per-kernel issue and wait counters of the headline run, and the ratios read from them."""
+    import csv
+    import glob
+    names = {}
+    for d in pmc_dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                names.setdefault(r["Counter_Name"], d)
+    per = {}
+    for c, d in names.items():
+        if c not in STALL_COUNTERS:
+            continue
+        for (k, grid), vals in _read_counter_csv(d, c).items():
+            if k.startswith("attn"):
+                per.setdefault((k, grid), {})[c] = sum(vals) / len(vals)
+    lines = ["# Issue and wait counters: attention fwd+bwd B4 H8 d128 T8192, non-causal", "",
+             "rocprofv3 counter passes (one per line of the command block; each pass stays within the per-block "
+             "counter limits) over the same run. Values are per dispatch, averaged over the dispatches of a "
+             "kernel and grid. The ratio columns: `co-issue` = SQ_VALU_MFMA_COEXEC_CYCLES / "
+             "SQ_VALU_MFMA_BUSY_CYCLES (share of matrix-busy cycles in which a VALU instruction issued too); "
+             "`wait`, `issue wait` and `active` = SQ_WAIT_ANY, SQ_WAIT_INST_ANY and SQ_ACTIVE_INST_ANY over "
+             "SQ_WAVE_CYCLES; `VALU/MFMA`, `SALU/MFMA` and `LDS/MFMA` = instruction counts per MFMA.", "",
+             "```", command or "", "```", "",
+             "| kernel | grid | co-issue | wait | issue wait | active | VALU/MFMA | SALU/MFMA | LDS/MFMA | "
+             "LDS bank conflicts |", "|---|---|---|---|---|---|---|---|---|---|"]
+
+    def ratio(cs, a, b, pct=True):
+        if a not in cs or b not in cs or cs[b] == 0:
+            return "-"
+        v = cs[a] / cs[b]
+        return f"{100 * v:.0f}%" if pct else f"{v:.2f}"
+
+    for (k, grid), cs in sorted(per.items()):
+        if not cs.get("SQ_INSTS_MFMA"):
+            continue
+        lines.append(f"| `{k}` | {grid} | {ratio(cs, 'SQ_VALU_MFMA_COEXEC_CYCLES', 'SQ_VALU_MFMA_BUSY_CYCLES')} | "
+                     f"{ratio(cs, 'SQ_WAIT_ANY', 'SQ_WAVE_CYCLES')} | {ratio(cs, 'SQ_WAIT_INST_ANY', 'SQ_WAVE_CYCLES')} | "
+                     f"{ratio(cs, 'SQ_ACTIVE_INST_ANY', 'SQ_WAVE_CYCLES')} | "
+                     f"{ratio(cs, 'SQ_INSTS_VALU', 'SQ_INSTS_MFMA', False)} | "
+                     f"{ratio(cs, 'SQ_INSTS_SALU', 'SQ_INSTS_MFMA', False)} | "
+                     f"{ratio(cs, 'SQ_INSTS_LDS', 'SQ_INSTS_MFMA', False)} | {cs.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+    lines += ["", "Raw values (per dispatch):", "", "| kernel | counter | value | meaning |", "|---|---|---|---|"]
+    for (k, grid), cs in sorted(per.items()):
+        for c in sorted(cs):
+            lines.append(f"| `{k}` | {c} | {cs[c]:.4g} | {STALL_COUNTERS[c]} |")
+    prof = out_dir or os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    path = os.path.join(prof, "fwd_bwd_d128_T8192_issue_counters.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    log(f"wrote {path}")
+
+
 def main():
     args = parse_args()
+    if args.summarize_stalls:
+        summarize_stalls(args.summarize_stalls, args.counter_command)
+        return
     if args.summarize_fp32:
         summarize_fp32(args.summarize_fp32, args.profile_command)
         return
