@@ -107,3 +107,24 @@ def test_fp32_summary_splits_full_and_causal_launches(tmp_path, steps):
     # 4 B H T^2 D = 2.749e11 flop in 2.2 ms; half of it in 1.25 ms when causal.
     assert "| fp32_d128_T4096_full | 3 | 2200.0 | 124.9 | 79% |" in md
     assert "| fp32_d128_T4096_causal | 3 | 1250.0 | 110.0 | 70% |" in md
+
+
+def test_issue_counter_summary_from_synthetic_passes(tmp_path):
+    """Ratios of the issue/wait summary, from two synthetic counter passes of
+    two dispatches each (the values are averaged per dispatch)."""
+    a, b, out = (str(tmp_path / n) for n in ("a", "b", "out"))
+    os.makedirs(out)
+    _counters(os.path.join(a, "run_counter_collection.csv"),
+              [(DKDV, d, 1048576, c, v) for d in (1, 2)
+               for c, v in (("SQ_WAVE_CYCLES", 1000.0), ("SQ_WAIT_ANY", 300.0), ("SQ_WAIT_INST_ANY", 250.0),
+                            ("SQ_ACTIVE_INST_ANY", 450.0))])
+    _counters(os.path.join(b, "run_counter_collection.csv"),
+              [(DKDV, d, 1048576, c, v) for d in (1, 2)
+               for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 3200.0), ("SQ_VALU_MFMA_COEXEC_CYCLES", 800.0),
+                            ("SQ_INSTS_MFMA", 100.0), ("SQ_INSTS_VALU", 460.0), ("SQ_INSTS_SALU", 230.0),
+                            ("SQ_INSTS_LDS", 150.0), ("SQ_LDS_BANK_CONFLICT", 0.0))])
+    bench.summarize_stalls([a, b], "pass a\npass b", out_dir=out)
+    md = open(os.path.join(out, "fwd_bwd_d128_T8192_issue_counters.md")).read()
+    # co-issue 800/3200, waits 300/1000 and 250/1000, active 450/1000, 4.6 / 2.3 / 1.5 per MFMA
+    assert "| `attn_dkdv_pair_kernel<128>` | 1048576 | 25% | 30% | 25% | 45% | 4.60 | 2.30 | 1.50 | 0 |" in md
+    assert "pass a\npass b" in md
