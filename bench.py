@@ -60,7 +60,8 @@ def parse_args():
                     help="also time plain bf16 GEMMs through torch (hipBLASLt) as a practical MFMA ceiling")
     ap.add_argument("--fp32-suite", action="store_true", help="time the fp32 grid (batch 4, 8 heads, head_dim 64/128)")
     ap.add_argument("--suites", action="store_true",
-                    help="also time the GQA suite (fwd+bwd, native GQA against repeated K/V) and the decode suite")
+                    help="also time the GQA suite (fwd+bwd, native GQA against repeated K/V), the decode suite, a head_dim "
+                         "sweep, the head_dim-64 grid and the KV-length case")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of this many MiB (reference dispatch for HBM counters)")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -570,6 +571,76 @@ def headdim_sweep(steps):
     return {"shape": "bf16 B4 H8 T4096 non-causal, fwd+bwd", "rows": rows}
 
 
+def config_grid(steps):
+    """The pages' head_dim-64 grid (bf16 B4 H8 d64, T in {512, 1024, 2048, 600, 1500, 3000}, causal and
+    not; fwd and fwd+bwd) and the KV-length case (bf16 B4 H8 d128 T4096, kv_len {1, 777, 2500, 4096},
+    fwd+bwd, TFLOP/s over both the nominal and the effective FLOPs, i.e. the keys inside each length)."""
+    import torch
+    from forward_backward_amd import attn
+    from forward_backward_amd.inputs import make_inputs, workload_cases
+    from forward_backward_amd.metrics import attention_flops, effective_flops
+
+    def fwd_ms(q, k, v, kw, n):
+        for _ in range(2):
+            attn.fwd(q, k, v, **kw)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            attn.fwd(q, k, v, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def step_ms(q, k, v, do, kw, n):
+        def step():
+            o, lse = attn.fwd(q, k, v, **kw)
+            return attn.bwd(q, k, v, o, lse, do, **kw)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = max(steps, 20)
+    rows = []
+    for case in workload_cases(1):
+        q = device_normal((case.B, case.Tq, case.Hq, case.D), 1)
+        k = device_normal((case.B, case.Tkv, case.Hkv, case.D), 2)
+        v = device_normal((case.B, case.Tkv, case.Hkv, case.D), 3)
+        do = device_normal((case.B, case.Tq, case.Hq, case.D), 4)
+        kw = dict(scale=case.scale, causal=case.causal)
+        f_ms, fb_ms = fwd_ms(q, k, v, kw, n), step_ms(q, k, v, do, kw, n)
+        ffl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, case.causal, "fwd")
+        fbfl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, case.causal, "fwd_bwd")
+        rows.append({"case": case.name, "fwd_ms": round(f_ms, 4), "fwd_tflops": round(ffl / (f_ms * 1e-3) / 1e12, 1),
+                     "fwd_bwd_ms": round(fb_ms, 4), "fwd_bwd_tflops": round(fbfl / (fb_ms * 1e-3) / 1e12, 1)})
+        log(f"  {case.name}: fwd {f_ms * 1e3:.1f} us ({rows[-1]['fwd_tflops']} TFLOP/s), fwd+bwd {fb_ms * 1e3:.1f} us "
+            f"({rows[-1]['fwd_bwd_tflops']} TFLOP/s)")
+        del q, k, v, do
+    (case,) = workload_cases(3)
+    lens = [int(x) for x in make_inputs(case, with_do=False)["kv_lens"]]
+    q = device_normal((case.B, case.Tq, case.Hq, case.D), 1)
+    k = device_normal((case.B, case.Tkv, case.Hkv, case.D), 2)
+    v = device_normal((case.B, case.Tkv, case.Hkv, case.D), 3)
+    do = device_normal((case.B, case.Tq, case.Hq, case.D), 4)
+    kl = torch.tensor(lens, dtype=torch.int32, device=q.device)
+    kw = dict(scale=case.scale, causal=False, kv_lens=kl)
+    fb_ms = step_ms(q, k, v, do, kw, n)
+    nominal = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, False, "fwd_bwd")
+    eff = effective_flops(case.Hq, case.Tq, lens, case.D, "fwd_bwd")
+    kvlen = {"case": case.name, "kv_lens": lens, "fwd_bwd_ms": round(fb_ms, 4),
+             "nominal_tflops": round(nominal / (fb_ms * 1e-3) / 1e12, 1),
+             "effective_tflops": round(eff / (fb_ms * 1e-3) / 1e12, 1)}
+    log(f"  {case.name} kv_lens {lens}: fwd+bwd {fb_ms:.3f} ms, {kvlen['effective_tflops']} TFLOP/s effective "
+        f"({kvlen['nominal_tflops']} nominal)")
+    return {"head_dim64_grid": {"shape": "bf16 B4 H8 d64", "rows": rows}, "kv_len": kvlen}
+
+
 FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 
 
@@ -863,6 +934,8 @@ def main():
         extra["decode_suite"] = decode_suite(50)
         log("head_dim sweep")
         extra["headdim_sweep"] = headdim_sweep(max(2, min(args.steps, 5)))
+        log("head_dim 64 grid and KV-length case")
+        extra["config_grid"] = config_grid(max(2, min(args.steps, 5)))
     if args.suites or args.fp32_suite:
         log("fp32 suite")
         extra["fp32_suite"] = fp32_suite(max(2, min(args.steps, 5)))

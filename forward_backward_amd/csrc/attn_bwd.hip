@@ -762,7 +762,7 @@ __global__ __launch_bounds__(256) void attn_dq_bf16_kernel(BwdArgs a) {
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, rank;
-  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank);
+  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank, a.Hq / a.Hkv);
   const int qt = nqt - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
@@ -1030,7 +1030,7 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, rank;
-  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank);
+  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank, a.Hq / a.Hkv);
   const int qt = nqt - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;

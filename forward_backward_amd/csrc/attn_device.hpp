@@ -274,19 +274,32 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // model). So the units are cut into groups, one per XCD when their number is
 // a multiple of 8, and each group issues its tiles rank by rank (longest
 // first) across its units.
-__device__ __forceinline__ void tile_order(int bid, int ntiles, int nunits, bool longest_first, int& unit,
-                                           int& t) {
+//
+// Either way each XCD receives a contiguous share of the unit ids, and units
+// can differ in cost (KV lengths per batch): the last batch's units would all
+// land on the last XCDs. So the ids are dealt out to the XCDs in turn: with
+// `together` consecutive units kept as one (the query heads of one KV head,
+// which share its K/V rows in L2) and their number S a multiple of 8, the i-th
+// super-unit of XCD x's share becomes super-unit x + 8 i.
+__device__ __forceinline__ void tile_order(int bid, int ntiles, int nunits, bool longest_first, int& unit, int& t,
+                                           int together = 1) {
   if (!longest_first) {
     unit = bid / ntiles;
     t = bid % ntiles;
-    return;
+  } else {
+    const int gsz = nunits >= 8 ? nunits / 8 : 1;     // units per group
+    const int g = bid / (gsz * ntiles);
+    const int gs = min(gsz, nunits - g * gsz);        // units in this group (the last may be short)
+    const int p = bid - g * gsz * ntiles;
+    t = p / gs;
+    unit = g * gsz + p % gs;
   }
-  const int gsz = nunits >= 8 ? nunits / 8 : 1;     // units per group
-  const int g = bid / (gsz * ntiles);
-  const int gs = min(gsz, nunits - g * gsz);        // units in this group (the last may be short)
-  const int p = bid - g * gsz * ntiles;
-  t = p / gs;
-  unit = g * gsz + p % gs;
+  const int nsu = together > 0 && nunits % together == 0 ? nunits / together : 0;
+  if (nsu >= 8 && nsu % 8 == 0) {
+    const int per = nsu / 8;                  // super-units per XCD
+    const int su = unit / together;
+    unit = ((su % per) * 8 + su / per) * together + unit % together;
+  }
 }
 
 __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int tkv) {

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_f32_kernel(FwdArgs a) {
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, rank;
-  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank);
+  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank, a.Hq / a.Hkv);
   const int qt = a.num_qtiles - 1 - rank;  // rank 0: the last query tile, the most keys when causal
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_dq_f32_kernel(BwdArg
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, rank;
-  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank);
+  tile_order(bid, nqt, a.B * a.Hq, a.causal, bh, rank, a.Hq / a.Hkv);
   const int qt = nqt - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, rank;
-  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank);
+  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank, a.Hq / a.Hkv);
   const int qt = a.num_qtiles - 1 - rank;  // rank 0: the last query tile, the most keys when causal
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(FwdPairCfg<D>::THREADS) void attn_fwd_pair_kernel(F
 
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int bh, rank;
-  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank);
+  tile_order(bid, a.num_qtiles, a.B * a.Hq, a.causal, bh, rank, a.Hq / a.Hkv);
   const int qt = a.num_qtiles - 1 - rank;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
