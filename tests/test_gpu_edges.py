@@ -203,3 +203,41 @@ def test_inputs_at_addresses_with_bit31_of_the_low_word_set():
     for a, b in zip(g_a, g_b):
         assert rel_err(to_host64(a), to_host64(b)) == 0.0
     del big
+
+
+def test_tensors_past_2_31_elements():
+    """Offsets past 2^31 elements: B = 16384, T = 1024, 2 query heads over one KV
+    head, head_dim 128 (K and V hold 2^31 elements each, Q, O and the gradients
+    2^32), with per-batch KV lengths. The inputs repeat 7 seeded batches along
+    the batch axis: batch b holds the data of batch b % 7. Those 7 are checked
+    against the oracle, and every batch's outputs must equal those of its
+    source batch bit for bit (the kernels' arithmetic does not depend on where
+    a batch sits), which an offset that wrapped at 2^31 or 2^32 would break."""
+    import torch
+    from forward_backward_amd import attn
+    small = Case("big_src_d128_T1024_gqa_kvlen", 7, 1024, 1024, 2, 1, 128,
+                 kv_lens=(1024, 1, 700, 0, 1000, 129, 513), workload_id=320)
+    host, dev, f64 = device_inputs(small)
+    B = 16384
+    print(f"[2^31 elements] B={B} T=1024 Hq=2 Hkv=1 d128", flush=True)
+    idx = torch.arange(B, device="cuda") % small.B
+    big = {n: torch.index_select(dev[n], 0, idx).contiguous() for n in ("q", "k", "v", "do")}
+    assert big["k"].numel() >= 2**31 and big["q"].numel() >= 2**32
+    lens = torch.index_select(dev["kv_lens"], 0, idx).contiguous()
+    o, lse = attn.fwd(big["q"], big["k"], big["v"], scale=small.scale, kv_lens=lens)
+    dq, dk, dv = attn.bwd(big["q"], big["k"], big["v"], o, lse, big["do"], scale=small.scale, kv_lens=lens)
+    torch.cuda.synchronize()
+    outs = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    for name, t in outs.items():
+        bits = t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+        same = torch.equal(bits, torch.index_select(bits[:small.B], 0, idx))
+        assert same, f"{name}: a batch differs from its source batch"
+    del big
+    ro, rlse = oracle.attention_fwd(f64["q"], f64["k"], f64["v"], small.scale, False, f64["kv_lens"])
+    rdq, rdk, rdv = oracle.attention_bwd(f64["q"], f64["k"], f64["v"], f64["do"], small.scale, False, f64["kv_lens"])
+    for name, g, r in (("o", o[:small.B], ro), ("dq", dq[:small.B], rdq), ("dk", dk[:small.B], rdk),
+                       ("dv", dv[:small.B], rdv)):
+        err = rel_err(to_host64(g), r)
+        print(f"    {name} rel err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], f"{name}: rel err {err:.3e}"
+    check_lse(to_host64(lse[:small.B]), rlse)
