@@ -80,3 +80,32 @@ def test_decode_is_deterministic():
     b = run_decode(case, dev)
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+def test_decode_caches_past_2_31_elements():
+    """Decode over K/V caches of 2^31 elements each (B = 64, 262144 keys, one KV
+    head, head_dim 128, 4 query heads, KV lengths per batch). Three seeded
+    batches repeat along the batch axis; they are checked against the oracle,
+    and every batch must equal its source bit for bit (equal lengths give equal
+    key ranges and the same combine order wherever the batch sits)."""
+    import torch
+    from forward_backward_amd import attn
+    small = Case("big_dec_src_kv262144", 3, 1, 262144, 4, 1, 128, kv_lens=(262144, 1, 100000), workload_id=321,
+                 decode=True)
+    host, dev, f64 = device_inputs(small, with_do=False)
+    B = 64
+    print(f"[decode 2^31 elements] B={B} keys={small.Tkv}", flush=True)
+    idx = torch.arange(B, device="cuda") % small.B
+    q, k, v = (torch.index_select(dev[n], 0, idx).contiguous() for n in ("q", "k", "v"))
+    assert k.numel() >= 2**31
+    lens = torch.index_select(dev["kv_lens"], 0, idx).contiguous()
+    o, lse = attn.decode(q, k, v, kv_lens=lens, scale=small.scale)
+    torch.cuda.synchronize()
+    for name, t, bits in (("o", o, o.view(torch.int16)), ("lse", lse, lse.view(torch.int32))):
+        assert torch.equal(bits, torch.index_select(bits[:small.B], 0, idx)), f"{name}: a batch differs from its source"
+    del k, v
+    ro, rlse = oracle.attention_decode(f64["q"], f64["k"], f64["v"], small.scale, f64["kv_lens"])
+    err = rel_err(to_host64(o[:small.B]), ro)
+    print(f"    o rel err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"], f"O rel err {err:.3e}"
+    check_lse(to_host64(lse[:small.B]), rlse)
