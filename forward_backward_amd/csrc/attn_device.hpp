@@ -252,6 +252,13 @@ __device__ __forceinline__ void dma_row64(float* dst, const float* g, int i0, in
 // Wait for this wave's outstanding global loads (including LDS DMA).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N), the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs of the chip; map the
 // hardware id to a logical id so that each XCD gets a contiguous range of
 // logical ids (neighbouring tiles of one head then share that XCD's L2).
