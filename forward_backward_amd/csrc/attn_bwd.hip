@@ -28,8 +28,6 @@ void launch_dq_bf16(const BwdArgs& a, int D, hipStream_t s);  // attn_dq.hip
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // ----------------------------------------------------------------- dK / dV
 //
 // One workgroup per (batch, KV head, 128 keys), 4 waves of 32 keys; K and V
@@ -384,12 +382,16 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
 //            dV^T += dO^T P
 //   dP wave: V rows and dK^T; dP = dO V^T, P from LDS,
 //            dS = P dP', dK^T += Q^T dS
-// Both roles run the same products: in step i the row product (S or dP) of
-// block i + 1 beside the transposed product (dV or dK) of block i, whose B
-// operand (P or dS) came from the previous step. One workgroup barrier per
-// step hands P over (double-buffered); the Q/dO/row-term ring is that of the
-// single-role kernel (three stages of 64-row tiles; the copy of tile t + 2
-// starts at step 2t and must have landed by the end of step 2t + 1).
+// At head_dim 256 (32-row tiles) both roles run the same products: in step i
+// the row product (S or dP) of block i + 1 beside the transposed product (dV
+// or dK) of block i, whose B operand (P or dS) came from the previous step; one
+// workgroup barrier per step hands P over (double-buffered). At head_dim 128
+// (64-row tiles of two blocks) a step covers a tile, with one barrier: the S
+// wave runs, block by block, the row product of tile j + 1 beside the
+// transposed product of tile j; the dP wave forms dP' and dS of tile j's blocks
+// in the step (P from the previous step, four hand-over slots). The Q/dO/
+// row-term ring is that of the single-role kernel (three stages; the copy of a
+// tile starts two tiles ahead and has landed by the end of the next step).
 template <int D>
 struct DkvPairCfg {
   // head_dim 128: 4 pairs (two waves per SIMD), 64-row tiles, 3 stages.
@@ -416,9 +418,13 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
   constexpr int R_OFF = 0;                        // row terms: 16 bytes per query row
   constexpr int Q_OFF = C::NST * C::BM * 16;      // Q stages
   constexpr int G_OFF = Q_OFF + C::NST * TB;      // dO stages
-  constexpr int X_OFF = G_OFF + C::NST * TB;      // P hand-over: [2][NP waves][2 halves][64 lanes] x 16 B
-  constexpr int XB = C::NP * 2 * 1024;            // bytes of one hand-over buffer
-  __shared__ __attribute__((aligned(16))) char smem[X_OFF + 2 * XB];
+  // With two 32-row blocks per tile (head_dim 128) a step covers a whole tile:
+  // both blocks between two barriers, their P in slots blk % 4.
+  constexpr bool TWO = C::BPT == 2;
+  constexpr int XN = TWO ? 4 : 2;                 // hand-over slots
+  constexpr int X_OFF = G_OFF + C::NST * TB;      // P hand-over: [XN][NP waves][2 halves][64 lanes] x 16 B
+  constexpr int XB = C::NP * 2 * 1024;            // bytes of one hand-over slot
+  __shared__ __attribute__((aligned(16))) char smem[X_OFF + XN * XB];
   uint16_t* const q_st = (uint16_t*)(smem + Q_OFF);
   uint16_t* const g_st = (uint16_t*)(smem + G_OFF);
   uint16_t* const r_st = (uint16_t*)(smem + R_OFF);
@@ -620,18 +626,82 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
         }
         pk[0] = pack8(pv);
         pk[1] = pack8(pv + 8);
-        const uint32_t xo = x_off + (blk & 1) * XB;
+        const uint32_t xo = x_off + (blk % XN) * XB;
         lds_write16((uint16_t*)(smem + xo), pk[0]);
         lds_write16((uint16_t*)(smem + xo + 1024), pk[1]);
       };
-      softmax(0, row_product(0));
+      if constexpr (TWO) {
+        // Step j: the transposed products of tile j's blocks 2j and 2j + 1
+        // (their P from the previous step) and the row products and softmax of
+        // tile j + 1's blocks, one block after the other, then one barrier.
+        u32x4_t pa[2], pb[2];
+        softmax(0, row_product(0));
+        pa[0] = pk[0];
+        pa[1] = pk[1];
+        softmax(1, row_product(1));
+        pb[0] = pk[0];
+        pb[1] = pk[1];
+        __syncthreads();
+        for (int j = 0; j < ntiles; ++j) {
+          if (j + 2 < ntiles) issue(j + 2);
+          f32x16_t s = row_product(2 * j + 2);
+          tr_product(2 * j, pa);
+          softmax(2 * j + 2, s);
+          pa[0] = pk[0];
+          pa[1] = pk[1];
+          __builtin_amdgcn_sched_barrier(0);  // one block's state live at a time
+          s = row_product(2 * j + 3);
+          tr_product(2 * j + 1, pb);
+          softmax(2 * j + 3, s);
+          pb[0] = pk[0];
+          pb[1] = pk[1];
+          wait_vmem();  // tile j + 2 (issued above) is read from the next step on
+          __syncthreads();
+        }
+      } else {
+        softmax(0, row_product(0));
+        __syncthreads();
+        for (int i = 0; i < nb; ++i) {
+          step_begin(i);
+          const f32x16_t s = row_product(i + 1);
+          tr_product(i, pk);
+          softmax(i + 1, s);
+          step_end(i);
+        }
+      }
+    } else if constexpr (TWO) {
+      auto ds_of = [&](int blk, const f32x16_t& dp, u32x4_t (&pk)[2]) {
+        const uint32_t xo = x_off + (blk % XN) * XB;
+        const u32x4_t p0 = lds_read16((const uint16_t*)(smem + xo));
+        const u32x4_t p1 = lds_read16((const uint16_t*)(smem + xo + 1024));
+        float dsv[16];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          dsv[2 * w] = bf16_lo(p0[w]) * dp[2 * w];
+          dsv[2 * w + 1] = bf16_hi(p0[w]) * dp[2 * w + 1];
+          dsv[8 + 2 * w] = bf16_lo(p1[w]) * dp[8 + 2 * w];
+          dsv[8 + 2 * w + 1] = bf16_hi(p1[w]) * dp[8 + 2 * w + 1];
+        }
+        pk[0] = pack8(dsv);
+        pk[1] = pack8(dsv + 8);
+      };
+      // Step j: tile j's blocks one after the other, dP' and dS formed in the
+      // step (P from the previous step): no dP' is carried over a barrier (two
+      // carried blocks spilled), and the partner's vector work fills the wait
+      // on each block's row product.
       __syncthreads();
-      for (int i = 0; i < nb; ++i) {
-        step_begin(i);
-        const f32x16_t s = row_product(i + 1);
-        tr_product(i, pk);
-        softmax(i + 1, s);
-        step_end(i);
+      for (int j = 0; j < ntiles; ++j) {
+        if (j + 2 < ntiles) issue(j + 2);
+        u32x4_t pk[2];
+        f32x16_t dp = row_product(2 * j);
+        ds_of(2 * j, dp, pk);
+        tr_product(2 * j, pk);
+        __builtin_amdgcn_sched_barrier(0);  // one block's state live at a time
+        dp = row_product(2 * j + 1);
+        ds_of(2 * j + 1, dp, pk);
+        tr_product(2 * j + 1, pk);
+        wait_vmem();  // tile j + 2 (issued above) is read from the next step on
+        __syncthreads();
       }
     } else {
       f32x16_t dp = row_product(0);
