@@ -294,7 +294,11 @@ struct DqPairCfg {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int R = 2;               // depth of the fragment read-ahead
-  static constexpr int NST = 3;             // K/V stages: tiles are copied two ahead
+  // Head_dim 64: two tiles per step and barrier (four stages: two read, two in
+  // flight); head_dim 128: one tile per step, copies two tiles ahead (three
+  // stages; the two-tile step measured 2% slower there at 256 registers).
+  static constexpr bool TWO = D <= 64;
+  static constexpr int NST = TWO ? 4 : 3;
   static constexpr int TILE = BN * D;
 };
 
@@ -369,10 +373,10 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
   }
 
   // Copies of tile `it` into stage `st`. They go through inline assembly, which
-  // the compiler does not see writing LDS: the waits before each tile's barrier
-  // order them (CP copy instructions per wave and tile, full or partial).
+  // the compiler does not see writing LDS: the waits before each step's
+  // barrier order them (CP copy instructions per wave and tile, full or partial).
   const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
-  constexpr int CP = 2 * TileCopy<D, C::BN, C::THREADS>::ITERS;
+  [[maybe_unused]] constexpr int CP = 2 * TileCopy<D, C::BN, C::THREADS>::ITERS;
   auto issue = [&](int it, int st) {
     uint16_t* ks = tiles + st * 2 * C::TILE;
     const int k0 = (j0 + it) * C::BN;
@@ -447,28 +451,54 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     }
   };
 
-  if (ntiles > 0) issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
-  // The Q and dO fragments and the first tiles have landed: without this the
-  // compiler, which only sees the fragment loads, waits for them inside the
-  // loop, where the wait would also drain the copies in flight.
-  wait_vmem();
-  int st_rd = 0, st_wr = 2;
-  for (int it = 0; it < ntiles; ++it) {
-    // Tile it has landed once at most the copies of tile it + 1 are in flight.
-    if (it + 1 < ntiles)
-      wait_vmcnt<CP>();
-    else
-      wait_vmem();
-    __syncthreads();  // tile it visible; every wave is done with tile it - 1, whose stage is refilled next
-    if (it + 2 < ntiles) issue(it + 2, st_wr);
-    const uint16_t* kl = tiles + st_rd * 2 * C::TILE;
-    const int k0 = (j0 + it) * C::BN;
-    const int kblk0 = k0 + 32 * half;
-    const bool mask = (kblk0 < wave_all_lo) || (kblk0 + 31 > wave_all_hi);
-    block(mask, kl, kl + C::TILE, kblk0);
-    st_rd = st_rd + 1 == C::NST ? 0 : st_rd + 1;
-    st_wr = st_wr + 1 == C::NST ? 0 : st_wr + 1;
+  if constexpr (C::TWO) {
+    // Two tiles per step and one barrier: tile t sits in stage t % 4; the
+    // copies of the next step's two tiles start after the step's barrier, once
+    // every wave is done with the two tiles before, and land before its end.
+    if (ntiles > 0) issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
+    // The Q and dO fragments and the first tiles have landed; waiting here also
+    // keeps the compiler, which only sees the fragment loads, from placing its
+    // own wait for them inside the loop.
+    wait_vmem();
+    for (int it = 0; it < ntiles; it += 2) {
+      __syncthreads();  // tiles it, it + 1 visible; tiles it - 2, it - 1 read by every wave
+      if (it + 2 < ntiles) issue(it + 2, (it + 2) % C::NST);
+      if (it + 3 < ntiles) issue(it + 3, (it + 3) % C::NST);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (u == 1 && it + 1 >= ntiles) break;
+        const uint16_t* kl = tiles + ((it + u) % C::NST) * 2 * C::TILE;
+        const int kblk0 = (j0 + it + u) * C::BN + 32 * half;
+        const bool mask = (kblk0 < wave_all_lo) || (kblk0 + 31 > wave_all_hi);
+        block(mask, kl, kl + C::TILE, kblk0);
+      }
+      wait_vmem();  // the next step's tiles have landed
+    }
+  } else {
+    if (ntiles > 0) issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
+    // The Q and dO fragments and the first tiles have landed: without this the
+    // compiler, which only sees the fragment loads, waits for them inside the
+    // loop, where the wait would also drain the copies in flight.
+    wait_vmem();
+    int st_rd = 0, st_wr = 2;
+    for (int it = 0; it < ntiles; ++it) {
+      // Tile it has landed once at most the copies of tile it + 1 are in flight.
+      if (it + 1 < ntiles)
+        wait_vmcnt<CP>();
+      else
+        wait_vmem();
+      __syncthreads();  // tile it visible; every wave is done with tile it - 1, whose stage is refilled next
+      if (it + 2 < ntiles) issue(it + 2, st_wr);
+      const uint16_t* kl = tiles + st_rd * 2 * C::TILE;
+      const int k0 = (j0 + it) * C::BN;
+      const int kblk0 = k0 + 32 * half;
+      const bool mask = (kblk0 < wave_all_lo) || (kblk0 + 31 > wave_all_hi);
+      block(mask, kl, kl + C::TILE, kblk0);
+      st_rd = st_rd + 1 == C::NST ? 0 : st_rd + 1;
+      st_wr = st_wr + 1 == C::NST ? 0 : st_wr + 1;
+    }
   }
 
   // The pair's partials: block-1 waves hand theirs over through LDS, block-0
