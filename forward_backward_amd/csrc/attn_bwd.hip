@@ -527,7 +527,11 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
              (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
     };
     // Byte offset of block `blk` (32 rows): its tile's stage and its place in the tile.
-    auto blk_off = [&](int blk) { return (uint32_t)(((blk / C::BPT) % C::NST) * TB + (blk % C::BPT) * BB); };
+    // (one wave-uniform value, so that each read adds it to its lane offset in
+    // one instruction)
+    auto blk_off = [&](int blk) {
+      return (uint32_t)__builtin_amdgcn_readfirstlane(((blk / C::BPT) % C::NST) * TB + (blk % C::BPT) * BB);
+    };
 
     // Row terms as one extra k-step (see the single-role kernel): the S wave
     // selects -LSE/scale, the dP wave -D.
