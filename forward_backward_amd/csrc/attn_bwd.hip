@@ -648,7 +648,11 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
         __syncthreads();
         for (int j = 0; j < ntiles; ++j) {
           if (j + 2 < ntiles) issue(j + 2);
+          // The S wave issues its row product at raised priority: its
+          // softmax, and through P the partner's next step, wait on it.
+          __builtin_amdgcn_s_setprio(1);
           f32x16_t s = row_product(2 * j + 2);
+          __builtin_amdgcn_s_setprio(0);
           tr_product(2 * j, pa);
           softmax(2 * j + 2, s);
           pa[0] = pk[0];
