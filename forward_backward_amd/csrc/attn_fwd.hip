@@ -250,10 +250,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     };
+    // At raised wave priority from head_dim 64 on: with two workgroups per
+    // compute unit, the wave running this interleaved phase is served before
+    // one running its PV products (at head_dim 32, three waves per SIMD, it
+    // measured slower).
+    if constexpr (D >= 64) __builtin_amdgcn_s_setprio(1);
     if (need_mask)
       body(std::true_type{});
     else
       body(std::false_type{});
+    if constexpr (D >= 64) __builtin_amdgcn_s_setprio(0);
     if (any) {
 #pragma unroll
       for (int i = 0; i < C::DB; ++i) o[i] *= alpha;
