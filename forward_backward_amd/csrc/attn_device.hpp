@@ -262,7 +262,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroups are dispatched round-robin over the 8 XCDs of the chip; map the
 // hardware id to a logical id so that each XCD gets a contiguous range of
 // logical ids (neighbouring tiles of one head then share that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   constexpr int kXcds = 8;
   const int q = n / kXcds, r = n % kXcds;
   const int x = bid % kXcds;
@@ -288,8 +288,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // `together` consecutive units kept as one (the query heads of one KV head,
 // which share its K/V rows in L2) and their number S a multiple of 8, the i-th
 // super-unit of XCD x's share becomes super-unit x + 8 i.
-__device__ __forceinline__ void tile_order(int bid, int ntiles, int nunits, bool longest_first, int& unit, int& t,
-                                           int together = 1) {
+__host__ __device__ __forceinline__ void tile_order(int bid, int ntiles, int nunits, bool longest_first, int& unit,
+                                                    int& t, int together = 1) {
   if (!longest_first) {
     unit = bid / ntiles;
     t = bid % ntiles;
