@@ -29,12 +29,15 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-# Per-source options. The dQ kernels are scheduled with LLVM's max-ILP
-# strategy: 2.7% faster at B4 H8 d128 T8192 (1.453 -> 1.414 ms, ten rounds
-# each) with the same registers. The other sources keep the default: there it
-# measured the same or made kernels spill or lose occupancy.
+# Per-source options. The dQ kernels and the head_dim 32-128 forward are
+# scheduled with LLVM's max-ILP strategy: dQ 2.7% faster at B4 H8 d128 T8192
+# (1.453 -> 1.414 ms, ten rounds each) with the same registers; the forward 1%
+# at head_dim 128 and 4% at 64, with one 8-byte spill outside its loop. The
+# other sources keep the default: there it measured the same or slower (the
+# head_dim 256 forward 7%), or made kernels spill or lose occupancy.
 PER_FILE = {
     "attn_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 
