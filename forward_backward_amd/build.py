@@ -35,9 +35,14 @@ COMMON = [
 # at head_dim 128 and 4% at 64, with one 8-byte spill outside its loop. The
 # other sources keep the default: there it measured the same or slower (the
 # head_dim 256 forward 7%), or made kernels spill or lose occupancy.
+# The head_dim 32/64 dK/dV kernel keeps its MFMA results in ordinary vector
+# registers (LLVM's choice was accumulation registers, read back with 32
+# v_accvgpr_read per step for the softmax): 13% faster at 32 and 9% at 64, same
+# occupancy. On the head_dim 256 kernels the same option measured 18% slower.
 PER_FILE = {
     "attn_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_dkdv_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
