@@ -121,7 +121,12 @@ __global__ __launch_bounds__(FwdPairCfg<D>::THREADS) void attn_fwd_pair_kernel(F
       qf[t] = row_ok ? gload16(qb + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
     int nrm[C::KS];
 #pragma unroll
-    for (int t = 0; t < C::KS; ++t) nrm[t] = swz_off<D>(l32, 16 * t + 8 * hh);
+    for (int t = 0; t < C::KS; ++t) {
+      // Byte offsets, opaque to the compiler: it would otherwise factor a
+      // common term out of them and add it back on every read.
+      nrm[t] = 2 * swz_off<D>(l32, 16 * t + 8 * hh);
+      asm volatile("" : "+v"(nrm[t]));
+    }
     float m = -INFINITY, lsum = 0.f;
     const int wave_min_row = q0 + 32 * w4;
     const int row_lo = key_lo(qrow, a.win_left);
@@ -131,15 +136,16 @@ __global__ __launch_bounds__(FwdPairCfg<D>::THREADS) void attn_fwd_pair_kernel(F
     for (int j = 0; j <= ntiles; ++j) {
       step_begin(j);
       if (j < ntiles) {
-        const uint16_t* kl = (const uint16_t*)(smem + (j % C::NST) * 2 * TB);
+        // The stage offset as one wave-uniform value: one vector add per read.
+        const char* kl = smem + __builtin_amdgcn_readfirstlane((j % C::NST) * 2 * TB);
         u32x4_t ka[C::R];
 #pragma unroll
-        for (int t = 0; t < C::R; ++t) ka[t] = lds_read16(kl + nrm[t]);
+        for (int t = 0; t < C::R; ++t) ka[t] = lds_read16((const uint16_t*)(kl + nrm[t]));
         f32x16_t s = f32x16_t{};
 #pragma unroll
         for (int t = 0; t < C::KS; ++t) {
           s = mfma_bf16(ka[t % C::R], qf[t], s);
-          if (t + C::R < C::KS) ka[t % C::R] = lds_read16(kl + nrm[t + C::R]);
+          if (t + C::R < C::KS) ka[t % C::R] = lds_read16((const uint16_t*)(kl + nrm[t + C::R]));
         }
         const int k0 = (j0 + j) * C::BN;
         if ((k0 < wave_all_lo) || (k0 + C::BN - 1 > wave_all_hi)) {
