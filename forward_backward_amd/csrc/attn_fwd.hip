@@ -243,11 +243,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     auto body = [&](auto mask_tag) {
       sdot(kn, s_nxt);
       any = softmax(mask_tag, j, s_cur, pf, alpha);
+      // Vector instructions per group: 6 at head_dim 128, 8 below (measured;
+      // 4, 5, 10 and 12 were slower at 128, and 6 slower at 32 and 64).
+      constexpr int VG = D == 128 ? 6 : 8;
 #pragma unroll
       for (int i = 0; i < 2 * C::KS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then vector ALU work
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, VG, 0);  // then vector ALU work
       }
       __builtin_amdgcn_sched_barrier(0);
     };
