@@ -107,10 +107,14 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _on_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _tensor4(name, t):
     if not isinstance(t, torch.Tensor) or t.dim() != 4:
         raise ValueError(f"{name} must be a 4-D tensor [B, T, H, D]")
-    if not t.is_cuda:
+    if not _on_device(t):
         raise ValueError(f"{name} must be on the GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -118,46 +122,91 @@ def _tensor4(name, t):
         raise ValueError(f"{name} must be bfloat16 or float32")
 
 
+def _like(name, t, shape, dtype, device):
+    """``t`` must be a contiguous tensor of exactly this shape and dtype on
+    ``device``: every pointer handed to the library covers what the kernels
+    read or write."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if not _on_device(t) or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(ws, need, device):
+    """A caller's workspace: contiguous device memory of at least ``need`` bytes.
+    Returns its size in bytes."""
+    if not isinstance(ws, torch.Tensor):
+        raise ValueError("workspace must be a tensor")
+    if not _on_device(ws) or ws.device != device:
+        raise ValueError(f"workspace must be on {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, {need} needed")
+    return nbytes
+
+
 def _params_for(q, k, scale, causal, kv_lens, window=None):
     _tensor4("q", q)
     _tensor4("k", k)
     if q.dtype != k.dtype:
         raise ValueError("q and k must share a dtype")
+    if k.device != q.device:
+        raise ValueError("q and k must be on the same GPU")
     if kv_lens is not None:
-        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != q.shape[0]:
-            raise ValueError("kv_lens must be a device int32 tensor of length B")
+        _like("kv_lens", kv_lens, (q.shape[0],), torch.int32, q.device)
     B, Tq, Hq, D = q.shape
     _, Tkv, Hkv, _ = k.shape
     return make_params(B, Tq, Tkv, Hq, Hkv, D, _DTYPES[q.dtype], scale, causal,
                        None if kv_lens is None else kv_lens.data_ptr(), window)
 
 
+def _lse_shape(p):
+    return (p.B, p.Hq, p.Tq)
+
+
 def fwd(q, k, v, scale=None, causal=False, kv_lens=None, out=None, lse=None, window=None):
     """O [B,Tq,Hq,D] (dtype of q) and LSE fp32 [B,Hq,Tq] via attn_fwd."""
     p = _params_for(q, k, scale, causal, kv_lens, window)
-    _tensor4("v", v)
-    if v.shape != k.shape or v.dtype != k.dtype:
-        raise ValueError("v must match k")
+    _like("v", v, k.shape, k.dtype, q.device)
     o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((p.B, p.Hq, p.Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    lse_t = torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device) if lse is None else lse
+    _like("out", o, q.shape, q.dtype, q.device)
+    _like("lse", lse_t, _lse_shape(p), torch.float32, q.device)
     _check(lib().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _stream()))
     return o, lse_t
+
+
+def _bwd_inputs(p, q, k, v=None, o=None, lse=None, do=None):
+    if v is not None:
+        _like("v", v, k.shape, k.dtype, q.device)
+    if o is not None:
+        _like("o", o, q.shape, q.dtype, q.device)
+    if lse is not None:
+        _like("lse", lse, _lse_shape(p), torch.float32, q.device)
+    if do is not None:
+        _like("do", do, q.shape, q.dtype, q.device)
 
 
 def bwd(q, k, v, o, lse, do, scale=None, causal=False, kv_lens=None, workspace=None, window=None):
     """dQ, dK, dV via attn_bwd (deterministic two-pass backward)."""
     p = _params_for(q, k, scale, causal, kv_lens, window)
-    for name, t, ref in (("v", v, k), ("o", o, q), ("do", do, q)):
-        _tensor4(name, t)
-        if t.shape != ref.shape or t.dtype != ref.dtype:
-            raise ValueError(f"{name} must match the shape and dtype of {'k' if ref is k else 'q'}")
+    _bwd_inputs(p, q, k, v, o, lse, do)
+    need = lib().attn_bwd_workspace_size(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nbytes = _workspace(ws, need, q.device)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    need = lib().attn_bwd_workspace_size(ctypes.byref(p))
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                          _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+                          _ptr(dk), _ptr(dv), _ptr(ws), nbytes, _stream()))
     return dq, dk, dv
 
 
@@ -171,32 +220,38 @@ def bwd_workspace(q, k, causal=False, kv_lens=None, window=None):
 def bwd_preprocess(o, lse, do, ws, q, k, scale=None, causal=False, kv_lens=None, window=None):
     """Pass 1 of the backward: D = rowsum(dO * O), LSE * log2(e) and the row terms into the workspace."""
     p = _params_for(q, k, scale, causal, kv_lens, window)
-    _check(lib().attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(lse), _ptr(do), _ptr(ws), ws.numel(),
-                                     _stream()))
+    _bwd_inputs(p, q, k, o=o, lse=lse, do=do)
+    nbytes = _workspace(ws, lib().attn_bwd_workspace_size(ctypes.byref(p)), q.device)
+    _check(lib().attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(lse), _ptr(do), _ptr(ws), nbytes, _stream()))
 
 
 def bwd_dkdv(q, k, v, lse, do, ws, dk, dv, scale=None, causal=False, kv_lens=None, window=None):
     """Pass 2 of the backward: dK and dV (needs the preprocess pass done)."""
     p = _params_for(q, k, scale, causal, kv_lens, window)
+    _bwd_inputs(p, q, k, v=v, lse=lse, do=do)
+    _like("dk", dk, k.shape, k.dtype, q.device)
+    _like("dv", dv, k.shape, k.dtype, q.device)
+    nbytes = _workspace(ws, lib().attn_bwd_workspace_size(ctypes.byref(p)), q.device)
     _check(lib().attn_bwd_dkdv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dk), _ptr(dv),
-                               _ptr(ws), ws.numel(), _stream()))
+                               _ptr(ws), nbytes, _stream()))
 
 
 def bwd_dq(q, k, v, lse, do, ws, dq, scale=None, causal=False, kv_lens=None, window=None):
     """Pass 3 of the backward: dQ (needs the preprocess pass done)."""
     p = _params_for(q, k, scale, causal, kv_lens, window)
+    _bwd_inputs(p, q, k, v=v, lse=lse, do=do)
+    _like("dq", dq, q.shape, q.dtype, q.device)
+    nbytes = _workspace(ws, lib().attn_bwd_workspace_size(ctypes.byref(p)), q.device)
     _check(lib().attn_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq), _ptr(ws),
-                             ws.numel(), _stream()))
+                             nbytes, _stream()))
 
 
 def decode(q, k_cache, v_cache, kv_lens=None, scale=None, num_splits=0, want_lse=True):
     """Split-KV decode: O [B,Tq,Hq,D] bf16 and LSE fp32 [B,Hq,Tq] (or None)."""
     p = _params_for(q, k_cache, scale, False, kv_lens)
-    _tensor4("v_cache", v_cache)
-    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
-        raise ValueError("v_cache must match k_cache")
+    _like("v_cache", v_cache, k_cache.shape, k_cache.dtype, q.device)
     o = torch.empty_like(q)
-    lse_t = torch.empty((p.B, p.Hq, p.Tq), dtype=torch.float32, device=q.device) if want_lse else None
+    lse_t = torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device) if want_lse else None
     need = lib().attn_decode_workspace_size(ctypes.byref(p), num_splits)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse_t),

@@ -6,6 +6,7 @@
 #include "../../include/attn.h"
 
 #include <cmath>
+#include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
@@ -19,8 +20,11 @@ namespace {
 
 thread_local char g_last_error[256] = "";
 
-attn_status_t fail(attn_status_t st, const char* fmt, int x = 0, int y = 0) {
-  std::snprintf(g_last_error, sizeof(g_last_error), fmt, x, y);
+__attribute__((format(printf, 2, 3))) attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
   return st;
 }
 
@@ -165,7 +169,7 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
   if (st != ATTN_OK) return st;
   const size_t need = attn_bwd_workspace_size(p);
   if (need > 0 && (ws == nullptr || ws_bytes < need))
-    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%d bytes needed)", (int)need);
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%zu bytes needed, %zu given)", need, ws_bytes);
   std::memset(&a, 0, sizeof(a));
   a.delta = static_cast<float*>(const_cast<void*>(ws));
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ws)) + bwd_stat_bytes(p));
@@ -294,7 +298,7 @@ attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_c
   if (num_splits == 0) num_splits = attn_decode_num_splits(p);
   const size_t need = attn_decode_workspace_size(p, num_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%d bytes needed)", (int)need);
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%zu bytes needed, %zu given)", need, workspace_bytes);
   const long segs = decode_segments(p);
   if ((long)num_splits + segs >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "too many splits");
   attn::DecodeArgs a;

@@ -1,10 +1,14 @@
 // Split-KV decode for few queries over a long KV cache, bf16, gfx950.
 //
-// probjax pages, "Attention performance", section "Grouped-query attention
-// and decoding": with few queries the regular kernel only parallelises over
-// batch x heads x query tiles; the split-KV forward instead splits the keys
-// across workgroups, packs the query heads of a GQA group into one tile and
-// combines the partial results with their log-sum-exp.
+// Method: probjax pages, "Attention performance", section "Grouped-query
+// attention and decoding". A handful of queries gives the tiled forward too
+// few workgroups (its grid is batch x heads x query tiles), so this path
+// divides each cache along its keys instead. One workgroup owns a key range
+// of one (batch, KV head) and all query rows that read that KV head, stacked
+// as one 64-row operand; each range yields a normalised partial output
+// with its log-sum-exp, and a second kernel merges the ranges of a row,
+// weighting each by its log-sum-exp. The range schedule, row packing and merge
+// order are described below.
 //
 // Packed row p = i * G + g is query i of query head KV_head * G + g. A
 // segment is one (batch, KV head, block of 64 packed rows); its n_b =

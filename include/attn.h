@@ -94,7 +94,9 @@ attn_status_t attn_validate(const attn_params_t* p, int32_t op);
 attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o,
                        float* lse, void* stream);
 
-/* Bytes of device workspace attn_bwd needs: per query row (B * Hq * Tq rows)
+/* Bytes of device workspace attn_bwd (and each of its passes) needs, for the
+ * row statistics of the split backward ("Attention performance", section
+ * "When to use which"): per query row (B * Hq * Tq rows)
  * 24 bytes, each region rounded up to 256 bytes: D = rowsum(dO * O) and
  * LSE * log2(e) (fp32 each), and 16 bytes of bf16 terms of -LSE/scale and -D
  * that the dK/dV pass adds to its products. With GQA (Hq > Hkv, bf16) and
@@ -106,10 +108,17 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
  * reproducible. */
 size_t attn_bwd_workspace_size(const attn_params_t* p);
 
-/* Backward: deterministic two-pass scheme without atomics. A pre-kernel
- * forms D = rowsum(dO * O) in the workspace; one kernel forms dK and dV per
- * KV tile (summing the G query heads of a group in a fixed order); one
- * kernel forms dQ per query tile. P is recomputed from `lse`.
+/* Backward: the gradients of a scalar loss with respect to Q, K and V given
+ * dO ("Attention performance", introduction). The pages' split backward is
+ * the scheme used here: a pass over key tiles for dK and dV and a separate
+ * pass over query tiles for dQ, which needs no atomic accumulation and so
+ * gives bitwise reproducible gradients ("Attention performance", section
+ * "When to use which"; "H100 (Hopper)", section "Why", where it is the
+ * robust choice). P is recomputed from the forward's `lse`, the residuals
+ * being O and LSE only ("Attention performance", section "Memory").
+ * A pre-kernel forms D = rowsum(dO * O) in the workspace; one kernel forms
+ * dK and dV per KV tile (summing the G query heads of a group in a fixed
+ * order); one kernel forms dQ per query tile.
  * q, k, v, o, lse as produced/consumed by attn_fwd; dout = dO like q.
  * dq like q; dk, dv like k. Keys at or past kv_lens[b] get dK = dV = 0.
  * Reruns on the same inputs are bitwise identical. */
@@ -118,7 +127,8 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        size_t workspace_bytes, void* stream);
 
 /* The three passes of attn_bwd as separate calls, in the order attn_bwd
- * runs them. attn_bwd_preprocess writes D = rowsum(dO * O) and LSE * log2(e)
+ * runs them (the split backward of "Attention performance", section "When
+ * to use which"). attn_bwd_preprocess writes D = rowsum(dO * O) and LSE * log2(e)
  * into the workspace; attn_bwd_dkdv and attn_bwd_dq read them and are
  * independent of each other, so a caller may run them on two streams once
  * the preprocess has completed. Arguments mean what they mean for attn_bwd. */
@@ -130,12 +140,16 @@ attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k
 attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
                           const void* dout, void* dq, const void* workspace, size_t workspace_bytes, void* stream);
 
-/* Split budget attn_decode uses when num_splits = 0: sized so that every key
+/* Split budget of the split-KV decode ("Attention performance", section
+ * "Grouped-query attention and decoding", where the keys are split because
+ * few queries leave the chip idle) when num_splits = 0: sized so that every key
  * range of the call runs at once on the chip (a pure function of the shape,
  * so reruns are bitwise identical). */
 int32_t attn_decode_num_splits(const attn_params_t* p);
 
-/* Bytes of device workspace attn_decode needs for the split budget
+/* Bytes of device workspace attn_decode needs, for the partial results of
+ * the split-KV decode ("Attention performance", section "Grouped-query
+ * attention and decoding"), for the split budget
  * `num_splits` (0 = auto): fp32 partial outputs and partial LSEs for at most
  * num_splits + B * Hkv * ceil(Tq * Hq / Hkv / 64) key ranges of 64 packed
  * rows each. */

@@ -1,20 +1,21 @@
 """Writes flop_convention.tsv from the raw benchmark JSON page of the probjax docs.
 
-Source: the page "gpu_attention_h100.json" (probjax benchmarks, H100), whose
-text is truncated mid-record; every complete record is kept.  The fixture
-stores, per record, the shape, mode, the median time in ms and the reported
-TFLOP/s, so that a test can check the FLOP convention used by bench.py
-against the pages' own numbers.  Run once by hand; the output is committed.
+Source: the probjax benchmark page "gpu_attention_h100.json" (NVIDIA H100),
+whose extracted text ends mid-record; every complete record is kept. The
+fixture stores, per record, the shape, mode, the median time in ms and the
+reported TFLOP/s, so that a test can check the FLOP convention used by
+bench.py against the pages' own numbers. Run once by hand with the path of a
+text copy of that page; the output is committed:
+
+    python tests/golden/extract_flop_records.py PAGE_TEXT [OUT_TSV]
 """
 import json
 import re
 import sys
 
-PAGE = "/root/reference/PAPER.md"
 
-
-def main(out_path):
-    text = open(PAGE, encoding="utf-8").read()
+def main(page_path, out_path):
+    text = open(page_path, encoding="utf-8").read()
     start = text.index('{ "device": { "jax"')
     body = text[start:]
     rows = []
@@ -36,4 +37,6 @@ def main(out_path):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1] if len(sys.argv) > 1 else "tests/golden/flop_convention.tsv")
+    if len(sys.argv) < 2:
+        sys.exit(__doc__)
+    main(sys.argv[1], sys.argv[2] if len(sys.argv) > 2 else "tests/golden/flop_convention.tsv")

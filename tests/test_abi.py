@@ -132,3 +132,130 @@ def test_status_strings():
     for s in range(5):
         assert L.attn_status_string(s)
     assert L.attn_status_string(99) == b"unknown status"
+
+
+class _Launched(Exception):
+    """Raised by the stand-in of a compute entry point: validation let the call through."""
+
+
+class _NoLaunchLib:
+    """The real library for host-only queries; every entry point that would
+    launch a kernel raises instead."""
+
+    COMPUTE = {"attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode"}
+
+    def __init__(self, real):
+        self._real = real
+
+    def __getattr__(self, name):
+        if name in self.COMPUTE:
+            def launch(*args):
+                raise _Launched(name)
+            return launch
+        return getattr(self._real, name)
+
+
+@pytest.fixture
+def host_binding(monkeypatch):
+    """The binding with host tensors standing in for device tensors and no launches."""
+    import torch
+    monkeypatch.setattr(attn, "_on_device", lambda t: True)
+    monkeypatch.setattr(attn, "_lib", _NoLaunchLib(attn.lib()))
+    monkeypatch.setattr(attn, "_stream", lambda: None)
+    return torch
+
+
+def _bwd_problem(torch, dtype=None):
+    dtype = dtype or torch.bfloat16
+    B, T, Hq, Hkv, D = 2, 64, 4, 2, 64
+    q = torch.zeros(B, T, Hq, D, dtype=dtype)
+    k = torch.zeros(B, T, Hkv, D, dtype=dtype)
+    lse = torch.zeros(B, Hq, T, dtype=torch.float32)
+    return q, k, lse
+
+
+def test_binding_lets_well_formed_calls_through(host_binding):
+    torch = host_binding
+    q, k, lse = _bwd_problem(torch)
+    v, o, do = torch.zeros_like(k), torch.zeros_like(q), torch.zeros_like(q)
+    for call in (lambda: attn.fwd(q, k, v),
+                 lambda: attn.bwd(q, k, v, o, lse, do),
+                 lambda: attn.bwd_dq(q, k, v, lse, do, attn.bwd_workspace(q, k), torch.zeros_like(q)),
+                 lambda: attn.bwd_dkdv(q, k, v, lse, do, attn.bwd_workspace(q, k), torch.zeros_like(k),
+                                       torch.zeros_like(k)),
+                 lambda: attn.bwd_preprocess(o, lse, do, attn.bwd_workspace(q, k), q, k),
+                 lambda: attn.decode(q[:, :4].contiguous(), k, v)):
+        with pytest.raises(_Launched):
+            call()
+
+
+def test_binding_rejects_every_malformed_tensor_before_any_launch(host_binding):
+    torch = host_binding
+    q, k, lse = _bwd_problem(torch)
+    v, o, do = torch.zeros_like(k), torch.zeros_like(q), torch.zeros_like(q)
+    ws = attn.bwd_workspace(q, k)
+    bad_lse = [lse.double(), lse[:, :, :-1], lse.transpose(1, 2).contiguous().transpose(1, 2), lse.to(torch.bfloat16)]
+    bad_q_like = [q.float(), q[:, :-1], q.transpose(1, 2), torch.zeros(2, 64, 4, 32, dtype=torch.bfloat16)]
+    bad_k_like = [k.float(), k[:, :-1], k.transpose(1, 2), torch.zeros_like(q)]
+    cases = []
+    for bl in bad_lse:
+        cases += [lambda bl=bl: attn.fwd(q, k, v, lse=bl),
+                  lambda bl=bl: attn.bwd(q, k, v, o, bl, do),
+                  lambda bl=bl: attn.bwd_preprocess(o, bl, do, ws, q, k),
+                  lambda bl=bl: attn.bwd_dkdv(q, k, v, bl, do, ws, torch.zeros_like(k), torch.zeros_like(k)),
+                  lambda bl=bl: attn.bwd_dq(q, k, v, bl, do, ws, torch.zeros_like(q))]
+    for bq in bad_q_like:
+        cases += [lambda bq=bq: attn.fwd(q, k, v, out=bq),
+                  lambda bq=bq: attn.bwd(q, k, v, bq, lse, do),
+                  lambda bq=bq: attn.bwd(q, k, v, o, lse, bq),
+                  lambda bq=bq: attn.bwd_preprocess(bq, lse, do, ws, q, k),
+                  lambda bq=bq: attn.bwd_preprocess(o, lse, bq, ws, q, k),
+                  lambda bq=bq: attn.bwd_dq(q, k, v, lse, bq, ws, torch.zeros_like(q)),
+                  lambda bq=bq: attn.bwd_dq(q, k, v, lse, do, ws, bq)]
+    for bk in bad_k_like:
+        cases += [lambda bk=bk: attn.fwd(q, k, bk),
+                  lambda bk=bk: attn.bwd(q, k, bk, o, lse, do),
+                  lambda bk=bk: attn.bwd_dkdv(q, k, bk, lse, do, ws, torch.zeros_like(k), torch.zeros_like(k)),
+                  lambda bk=bk: attn.bwd_dkdv(q, k, v, lse, do, ws, bk, torch.zeros_like(k)),
+                  lambda bk=bk: attn.bwd_dkdv(q, k, v, lse, do, ws, torch.zeros_like(k), bk),
+                  lambda bk=bk: attn.bwd_dq(q, k, bk, lse, do, ws, torch.zeros_like(q)),
+                  lambda bk=bk: attn.decode(q, k, bk)]
+    small_ws = ws[:-1]
+    cases += [lambda: attn.bwd(q, k, v, o, lse, do, workspace=small_ws),
+              lambda: attn.bwd_preprocess(o, lse, do, small_ws, q, k),
+              lambda: attn.bwd_dkdv(q, k, v, lse, do, small_ws, torch.zeros_like(k), torch.zeros_like(k)),
+              lambda: attn.bwd_dq(q, k, v, lse, do, small_ws, torch.zeros_like(q)),
+              lambda: attn.bwd_dq(q, k, v, lse, do, ws[::2], torch.zeros_like(q)),
+              lambda: attn.bwd_dq(q, k, v, lse, do, "not a tensor", torch.zeros_like(q)),
+              lambda: attn.fwd(q, k, v, kv_lens=torch.zeros(2, dtype=torch.int64)),
+              lambda: attn.fwd(q, k, v, kv_lens=torch.zeros(3, dtype=torch.int32)),
+              lambda: attn.fwd(q, k, v, kv_lens=torch.zeros(2, 1, dtype=torch.int32))]
+    for i, call in enumerate(cases):
+        with pytest.raises(ValueError):
+            call()
+
+
+def test_binding_counts_workspace_bytes_not_elements(host_binding):
+    torch = host_binding
+    q, k, lse = _bwd_problem(torch)
+    need = attn.lib().attn_bwd_workspace_size(ctypes.byref(attn.make_params(2, 64, 64, 4, 2, 64)))
+    ws32 = torch.zeros((need + 3) // 4, dtype=torch.float32)  # enough bytes in fewer elements
+    with pytest.raises(_Launched):
+        attn.bwd_dq(q, k, torch.zeros_like(k), lse, torch.zeros_like(q), ws32, torch.zeros_like(q))
+
+
+def test_workspace_errors_report_sizes_above_2_gib():
+    """Workspace sizes print as size_t: a 12 GiB backward workspace and a
+    decode workspace past 2^32 bytes are quoted exactly."""
+    L = attn.lib()
+    p = P(B=1024, Tq=65536, Tkv=65536, Hq=8, Hkv=8)
+    need = L.attn_bwd_workspace_size(ctypes.byref(p))
+    assert need == 6 * 1024 * 8 * 65536 * 4 > 2**33
+    assert L.attn_bwd(ctypes.byref(p), *([FAKE] * 9), FAKE, 1, None) == attn.ATTN_ERR_WORKSPACE
+    assert f"{need} bytes needed, 1 given".encode() in L.attn_last_error()
+    d = P(B=65536, Tq=1, Tkv=1024, Hq=32, Hkv=8)
+    wneed = L.attn_decode_workspace_size(ctypes.byref(d), 0)
+    assert wneed > 2**32
+    assert L.attn_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, wneed - 16, None) == \
+        attn.ATTN_ERR_WORKSPACE
+    assert f"{wneed} bytes needed, {wneed - 16} given".encode() in L.attn_last_error()

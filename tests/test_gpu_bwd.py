@@ -1,11 +1,13 @@
-"""Backward parity of the HIP kernels against the float64 oracle (needs an MI355X)."""
+"""Backward parity of the HIP kernels against the float64 oracle on small and
+ragged shapes, determinism and the split passes (needs an MI355X); the five
+workloads are compared in full in test_gpu_workloads.py."""
 
 import numpy as np
 import pytest
 
 import oracle
-from forward_backward_amd.inputs import Case, workload_cases
-from helpers import TOL, device_inputs, rel_err, to_host64
+from forward_backward_amd.inputs import Case
+from helpers import TOL, ZERO_TOL, device_inputs, rel_err, to_host64
 from test_gpu_fwd import SMALL
 
 pytestmark = pytest.mark.gpu
@@ -20,27 +22,21 @@ def run_fwd_bwd(case, dev):
     return o, lse, dq, dk, dv
 
 
-def check_bwd(case, kv_heads=None):
+def check_bwd(case, zero_tol=ZERO_TOL):
+    """Forward and backward on the GPU, dQ, dK and dV of every head against the oracle.
+    ``zero_tol``: the absolute bound on a gradient whose exact value is zero everywhere."""
     import torch
     host, dev, f64 = device_inputs(case)
     print(f"[bwd] {case.name}", flush=True)
     _, _, dq, dk, dv = run_fwd_bwd(case, dev)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle.attention_bwd(f64["q"], f64["k"], f64["v"], f64["do"], case.scale, case.causal,
-                                         f64["kv_lens"], kv_heads=kv_heads, window=case.window)
+                                         f64["kv_lens"], window=case.window)
     gdq, gdk, gdv = to_host64(dq), to_host64(dk), to_host64(dv)
-    if kv_heads is not None:
-        G = case.Hq // case.Hkv
-        sel = lambda x, y: (np.stack([x[b, :, kh * G:(kh + 1) * G] for b, kh in kv_heads]),  # noqa: E731
-                            np.stack([y[b, :, kh * G:(kh + 1) * G] for b, kh in kv_heads]))
-        selk = lambda x, y: (np.stack([x[b, :, kh] for b, kh in kv_heads]),  # noqa: E731
-                             np.stack([y[b, :, kh] for b, kh in kv_heads]))
-        pairs = {"dq": sel(gdq, rdq), "dk": selk(gdk, rdk), "dv": selk(gdv, rdv)}
-    else:
-        pairs = {"dq": (gdq, rdq), "dk": (gdk, rdk), "dv": (gdv, rdv)}
+    pairs = {"dq": (gdq, rdq), "dk": (gdk, rdk), "dv": (gdv, rdv)}
     for name, (g, r) in pairs.items():
-        err = rel_err(g, r)
-        print(f"    {name} rel err {err:.3e}", flush=True)
+        err = rel_err(g, r, zero_tol)
+        print(f"    {name} rel err {err:.3e} (max|got| {np.abs(g).max() if g.size else 0:.3e})", flush=True)
         assert err <= TOL[case.dtype], f"{case.name}: {name} rel err {err:.3e}"
     if case.kv_lens is not None:
         for b, n in enumerate(case.kv_lens):
@@ -55,16 +51,6 @@ def test_bwd_small(case):
     check_bwd(case)
 
 
-def test_bwd_fp32_correctness_workload():
-    (case,) = workload_cases(0)
-    check_bwd(case)
-
-
-@pytest.mark.parametrize("case", workload_cases(1), ids=lambda c: c.name)
-def test_bwd_bf16_d64_grid_sampled(case):
-    check_bwd(case, kv_heads=[(0, 0), (3, 7), (1, 4)])
-
-
 def test_bwd_is_bitwise_deterministic():
     import torch
     case = Case("d128_T333_causal_gqa_kvlen", 2, 333, 333, 8, 2, 128, causal=True, kv_lens=(333, 200),
@@ -76,19 +62,6 @@ def test_bwd_is_bitwise_deterministic():
         for a, b in zip(runs[0], r):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
-
-
-@pytest.mark.parametrize("case", workload_cases(2), ids=lambda c: c.name)
-def test_bwd_headline_T8192_sampled(case):
-    check_bwd(case, kv_heads=[(0, 0), (3, 5)])
-
-
-def test_bwd_kv_length_workload_sampled():
-    (case,) = workload_cases(3)
-    dq, dk, _ = check_bwd(case, kv_heads=[(0, 1), (1, 0), (2, 7), (3, 3)])
-    # Batch 0 has a single valid key: the exact dQ and dK are zero.
-    assert float(to_host64(dq[0]).__abs__().max()) <= 1e-3
-    assert float(to_host64(dk[0]).__abs__().max()) <= 1e-3
 
 
 @pytest.mark.parametrize("case", [

@@ -6,7 +6,6 @@ Tq != Tkv and local windows, plus the pages' fp32 grid shape (batch 4, 8
 heads, T = 4096) on sampled heads. Tolerance: max|a - b| / max|b| <= 1e-4.
 """
 
-import numpy as np
 import pytest
 
 from forward_backward_amd.inputs import Case, workload_cases
@@ -45,10 +44,9 @@ SCALE = {c.name: c for c in workload_cases(8)}
 
 
 @pytest.mark.parametrize("name", ["fp32_d128_T4096_full", "fp32_d64_T4096_causal"])
-def test_fp32_grid_sampled(name):
-    case = SCALE[name]
-    check_case(case, heads=[(0, 0), (3, 5)])
-    check_bwd(case, kv_heads=[(1, 2)])
+def test_fp32_grid_full(name):
+    from test_gpu_workloads import check_workload
+    check_workload(SCALE[name])
 
 
 def test_fp32_is_deterministic():

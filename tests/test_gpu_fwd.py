@@ -1,10 +1,12 @@
-"""Forward parity of the HIP kernels against the float64 oracle (needs an MI355X)."""
+"""Forward parity of the HIP kernels against the float64 oracle on small and
+ragged shapes (needs an MI355X); the five workloads are compared in full in
+test_gpu_workloads.py."""
 
 import numpy as np
 import pytest
 
 import oracle
-from forward_backward_amd.inputs import Case, workload_cases
+from forward_backward_amd.inputs import Case
 from helpers import TOL, check_lse, device_inputs, rel_err, to_host64
 
 pytestmark = pytest.mark.gpu
@@ -32,25 +34,19 @@ def run_fwd(case, dev):
                     window=case.window)
 
 
-def check_case(case, heads=None):
+def check_case(case):
+    """Forward on the GPU, O and LSE of every head against the oracle."""
     import torch
     host, dev, f64 = device_inputs(case, with_do=False)
     print(f"[fwd] {case.name}", flush=True)
     o, lse = run_fwd(case, dev)
     torch.cuda.synchronize()
-    ro, rlse = oracle.attention_fwd(f64["q"], f64["k"], f64["v"], case.scale, case.causal, f64["kv_lens"], heads=heads,
+    ro, rlse = oracle.attention_fwd(f64["q"], f64["k"], f64["v"], case.scale, case.causal, f64["kv_lens"],
                                     window=case.window)
     go, glse = to_host64(o), to_host64(lse)
-    if heads is not None:
-        sel_o = np.stack([go[b, :, h] for b, h in heads])
-        ref_o = np.stack([ro[b, :, h] for b, h in heads])
-        sel_l = np.stack([glse[b, h] for b, h in heads])
-        ref_l = np.stack([rlse[b, h] for b, h in heads])
-    else:
-        sel_o, ref_o, sel_l, ref_l = go, ro, glse, rlse
-    err = rel_err(sel_o, ref_o)
+    err = rel_err(go, ro)
     assert err <= TOL[case.dtype], f"{case.name}: O rel err {err:.3e}"
-    check_lse(sel_l, ref_l)
+    check_lse(glse, rlse)
     # rows without a valid key are exactly zero
     if case.kv_lens is not None:
         for b, n in enumerate(case.kv_lens):
@@ -64,16 +60,6 @@ def test_fwd_small(case):
     check_case(case)
 
 
-def test_fwd_fp32_correctness_workload():
-    (case,) = workload_cases(0)
-    check_case(case)
-
-
-@pytest.mark.parametrize("case", workload_cases(1), ids=lambda c: c.name)
-def test_fwd_bf16_d64_grid_sampled(case):
-    check_case(case, heads=[(0, 0), (3, 7), (1, 4)])
-
-
 def test_fwd_is_deterministic():
     import torch
     case = SMALL[7]
@@ -83,12 +69,3 @@ def test_fwd_is_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
-
-@pytest.mark.parametrize("case", workload_cases(2), ids=lambda c: c.name)
-def test_fwd_headline_T8192_sampled(case):
-    check_case(case, heads=[(0, 0), (3, 5)])
-
-
-def test_fwd_kv_length_workload_sampled():
-    (case,) = workload_cases(3)
-    check_case(case, heads=[(0, 1), (1, 0), (2, 7), (3, 3)])

@@ -39,11 +39,10 @@ def test_d256_bwd(case):
     check_bwd(case)
 
 
-def test_d256_B2_H16_T2048_sampled():
+def test_d256_B2_H16_T2048_full():
     # 2 * 16 * 16 = 512 dK/dV workgroups: no head split; all passes at full tiles
-    case = Case("d256_B2_H16_T2048", 2, 2048, 2048, 16, 16, 256, workload_id=505)
-    check_case(case, heads=[(0, 0), (1, 15)])
-    check_bwd(case, kv_heads=[(0, 3), (1, 15)])
+    from test_gpu_workloads import check_workload
+    check_workload(Case("d256_B2_H16_T2048", 2, 2048, 2048, 16, 16, 256, workload_id=505))
 
 
 @pytest.mark.parametrize("case", [

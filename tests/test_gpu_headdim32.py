@@ -35,10 +35,9 @@ def test_d32_bwd(case):
     check_bwd(case)
 
 
-def test_d32_B4_H8_T2048_sampled():
-    case = Case("d32_B4_H8_T2048", 4, 2048, 2048, 8, 8, 32, workload_id=406)
-    check_case(case, heads=[(0, 0), (3, 7)])
-    check_bwd(case, kv_heads=[(0, 0), (3, 7)])
+def test_d32_B4_H8_T2048_full():
+    from test_gpu_workloads import check_workload
+    check_workload(Case("d32_B4_H8_T2048", 4, 2048, 2048, 8, 8, 32, workload_id=406))
 
 
 @pytest.mark.parametrize("case", [

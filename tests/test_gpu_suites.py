@@ -8,12 +8,10 @@ head_dim 128, 8 or 32 KV heads, full caches.
 import numpy as np
 import pytest
 
-import oracle
 from forward_backward_amd.inputs import workload_cases
 from helpers import TOL, check_lse, device_inputs, rel_err, to_host64
-from test_gpu_bwd import check_bwd, run_fwd_bwd
+from test_gpu_bwd import run_fwd_bwd
 from test_gpu_decode import check_decode
-from test_gpu_fwd import check_case
 
 pytestmark = pytest.mark.gpu
 
@@ -22,11 +20,9 @@ DECODE = {(c.B, c.Tkv, c.Hkv): c for c in workload_cases(6)}
 
 
 @pytest.mark.parametrize("T", [2048, 4096])
-def test_gqa_suite_fwd_bwd_sampled(T):
-    case = GQA[T]
-    # KV head 0 and KV head 5 with all four of their query heads.
-    check_case(case, heads=[(0, h) for h in (0, 1, 2, 3, 20, 21, 22, 23)])
-    check_bwd(case, kv_heads=[(0, 0), (0, 5)])
+def test_gqa_suite_fwd_bwd_full(T):
+    from test_gpu_workloads import check_workload
+    check_workload(GQA[T])
 
 
 def test_gqa_suite_native_equals_repeated_kv():
