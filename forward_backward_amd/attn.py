@@ -64,6 +64,7 @@ _SIGS = {
     "attn_decode_num_splits": (ctypes.c_int32, [_P]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [_P, ctypes.c_int32]),
     "attn_decode": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_int32, _V, ctypes.c_size_t, _V]),
+    "attn_decode_noalloc": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_int32, _V]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_last_error": (ctypes.c_char_p, []),
 }
@@ -256,6 +257,24 @@ def decode(q, k_cache, v_cache, kv_lens=None, scale=None, num_splits=0, want_lse
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib().attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse_t),
                              num_splits, _ptr(ws), ws.numel(), _stream()))
+    return o, lse_t
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_lens=None, scale=None, num_splits=0, out=None, lse=None,
+                   want_lse=True):
+    """Split-KV decode through attn_decode_noalloc: the library's static
+    scratch replaces the workspace, so with ``out`` (and ``lse``) given the
+    call allocates nothing."""
+    p = _params_for(q, k_cache, scale, False, kv_lens)
+    _like("v_cache", v_cache, k_cache.shape, k_cache.dtype, q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = lse if lse is not None else (torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device)
+                                         if want_lse else None)
+    _like("out", o, q.shape, q.dtype, q.device)
+    if lse_t is not None:
+        _like("lse", lse_t, _lse_shape(p), torch.float32, q.device)
+    _check(lib().attn_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse_t),
+                                     num_splits, _stream()))
     return o, lse_t
 
 

@@ -286,8 +286,14 @@ size_t attn_decode_workspace_size(const attn_params_t* p, int32_t num_splits) {
   return round_up(rows * (size_t)p->D * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
-attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache, void* o,
-                          float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a decode call that need no device (arguments, split budget);
+// fills `num_splits` (0 = automatic resolved) and the workspace size needed.
+attn_status_t decode_check(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache,
+                           const void* o, int32_t& num_splits, size_t& need) {
   attn_status_t st = attn_validate(p, ATTN_OP_DECODE);
   if (st != ATTN_OK) return st;
   const Sizes n = sizes_of(p);
@@ -296,11 +302,15 @@ attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_c
     return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   if (num_splits < 0) return fail(ATTN_ERR_INVALID, "num_splits must be >= 0 (0 = automatic)");
   if (num_splits == 0) num_splits = attn_decode_num_splits(p);
-  const size_t need = attn_decode_workspace_size(p, num_splits);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%zu bytes needed, %zu given)", need, workspace_bytes);
+  if ((long)num_splits + decode_segments(p) >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "too many splits");
+  need = attn_decode_workspace_size(p, num_splits);
+  return ATTN_OK;
+}
+
+// Launches of a checked decode call with its workspace.
+attn_status_t decode_run(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache, void* o,
+                         float* lse, int32_t num_splits, void* workspace, void* stream) {
   const long segs = decode_segments(p);
-  if ((long)num_splits + segs >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "too many splits");
   attn::DecodeArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_lens = p->kv_lens;
   const size_t rows = (size_t)(num_splits + segs) * attn::kDecodeRows;
@@ -314,6 +324,36 @@ attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_c
   hipError_t e = attn::launch_decode_bf16(a, p->D, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache, void* o,
+                          float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  attn_status_t st = decode_check(p, q, k_cache, v_cache, o, num_splits, need);
+  if (st != ATTN_OK) return st;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small (%zu bytes needed, %zu given)", need, workspace_bytes);
+  return decode_run(p, q, k_cache, v_cache, o, lse, num_splits, workspace, stream);
+}
+
+attn_status_t attn_decode_noalloc(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache,
+                                  void* o, float* lse, int32_t num_splits, void* stream) {
+  size_t need = 0;
+  attn_status_t st = decode_check(p, q, k_cache, v_cache, o, num_splits, need);
+  if (st != ATTN_OK) return st;
+  if (need > ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(ATTN_ERR_WORKSPACE, "needs %zu bytes of scratch; the library's static scratch holds %zu",
+                need, (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = attn::decode_scratch(&scratch);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "static scratch unavailable (hip error %d)", (int)e);
+  }
+  return decode_run(p, q, k_cache, v_cache, o, lse, num_splits, scratch, stream);
 }
 
 const char* attn_status_string(attn_status_t status) {

@@ -31,6 +31,9 @@
 // in ascending order with a running maximum: LSE = log sum_r exp(LSE_r),
 // O = sum_r exp(LSE_r - LSE) O_r. A row with no valid key gets O = 0 and
 // LSE = -inf.
+#include <mutex>
+
+#include "../../include/attn.h"
 #include "attn_device.hpp"
 #include "attn_internal.h"
 
@@ -428,6 +431,36 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// Scratch of attn_decode_noalloc: the partial outputs and LSEs of the key
+// ranges, in place of a caller's workspace. Each device holds its own copy of
+// the array until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device below and only that address is handed to kernels. Calls that
+// overlap on one device share the array and race.
+static __device__ __align__(256) char scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s) {
   if (D == 128)

@@ -76,6 +76,10 @@ enum BwdPass { kBwdPre = 0, kBwdDkdv = 1, kBwdDq = 2 };
 hipError_t launch_bwd_pass_bf16(const BwdArgs& a, int D, int pass, hipStream_t s);
 hipError_t launch_bwd_pass_fp32(const BwdArgs& a, int D, int pass, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int D, hipStream_t s);
+// Device address of the decode's static scratch on the current device (the
+// array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES in attn_decode.hip), looked up
+// once per device.
+hipError_t decode_scratch(void** ptr);
 
 // Tile sizes the host needs for grids and workspaces.
 constexpr int kFwdBlockM = 128;   // query rows per forward workgroup

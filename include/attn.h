@@ -176,6 +176,22 @@ attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_c
                           void* o, float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Bytes of device memory behind attn_decode_noalloc on each device. */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments and results as attn_decode (the same
+ * kernels, bit for bit); the partial results live in a static device array of
+ * ATTN_DECODE_NOALLOC_SCRATCH_BYTES per device, held until the process ends.
+ * A call whose workspace (attn_decode_workspace_size for its split budget)
+ * exceeds that returns ATTN_ERR_WORKSPACE before touching the device. The
+ * call allocates and frees nothing; its first call on a device looks up the
+ * array's device address. Every call on one device shares the array:
+ * calls that overlap on one device (several streams or threads) race. */
+attn_status_t attn_decode_noalloc(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache,
+                                  void* o, float* lse, int32_t num_splits, void* stream);
+
 /* Static description of a status code. */
 const char* attn_status_string(attn_status_t status);
 

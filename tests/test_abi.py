@@ -259,3 +259,22 @@ def test_workspace_errors_report_sizes_above_2_gib():
     assert L.attn_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, wneed - 16, None) == \
         attn.ATTN_ERR_WORKSPACE
     assert f"{wneed} bytes needed, {wneed - 16} given".encode() in L.attn_last_error()
+
+
+def test_noalloc_decode_rejects_oversized_calls_before_touching_a_device():
+    """Calls whose workspace would exceed the static scratch are refused on the
+    host, and so are malformed ones, with no HIP call made (none is possible here)."""
+    L = attn.lib()
+    d = P(B=8, Tq=256, Tkv=65536, Hq=32, Hkv=32)  # 8 * 32 * 4 row blocks = 1024 segments
+    need = L.attn_decode_workspace_size(ctypes.byref(d), 0)
+    assert need > (32 << 20)
+    assert L.attn_decode_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, None) == attn.ATTN_ERR_WORKSPACE
+    assert f"needs {need} bytes of scratch".encode() in L.attn_last_error()
+    assert f"holds {32 << 20}".encode() in L.attn_last_error()
+    ok = P(Tq=16, Tkv=16384, Hq=32, Hkv=8)
+    assert L.attn_decode_noalloc(ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, None, 2**30, None) == \
+        attn.ATTN_ERR_WORKSPACE
+    assert L.attn_decode_noalloc(ctypes.byref(ok), None, FAKE, FAKE, FAKE, None, 0, None) == attn.ATTN_ERR_INVALID
+    assert L.attn_decode_noalloc(ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, None, -1, None) == attn.ATTN_ERR_INVALID
+    assert L.attn_decode_noalloc(ctypes.byref(P(causal=True)), FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
+        attn.ATTN_ERR_INVALID
