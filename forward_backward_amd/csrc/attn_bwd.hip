@@ -178,18 +178,49 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
         dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
       }
     };
+    // In-order issue of the tiles (TWO path): tile t is query tile
+    // qt_begin + t % nq of head h_lo + t / nq, and the copies go out for
+    // t = 0, 1, ... in turn, so the tile, head and stage counters advance by
+    // one per call instead of being divided out of t.
+    int iss_q = 0, iss_st = 0;
+    const long hbase = (long)b * a.Tq * a.Hq + kh * G + h_lo;
+    const uint16_t* iss_qh = (const uint16_t*)a.q + hbase * D;
+    const uint16_t* iss_gh = (const uint16_t*)a.dout + hbase * D;
+    const uint16_t* iss_rh = a.rowstat + (((long)b * a.Hq + kh * G + h_lo) * a.Tq) * 8;
+    auto issue_next = [&]() {
+      const int q0 = (qt_begin + iss_q) * C::BM;
+      uint16_t* qs = q_st + iss_st * C::TILE;
+      if (q0 + C::BM <= a.Tq) {
+        qcopy.template copy2<G_OFF - Q_OFF>(qs, iss_qh, iss_gh, qrs, q0);
+      } else {
+        dma_tile<D, C::BM, C::THREADS>(qs, iss_qh, qrs, q0, a.Tq, tid);
+        dma_tile<D, C::BM, C::THREADS>(g_st + iss_st * C::TILE, iss_gh, qrs, q0, a.Tq, tid);
+      }
+      if (wave == 0 && lane < C::BM) {
+        const int i = min(q0 + lane, a.Tq - 1);
+        dma16(iss_rh + (long)i * 8, lds_addr(r_st + iss_st * C::BM * 8));
+      }
+      iss_st = iss_st + 1 == C::NST ? 0 : iss_st + 1;
+      if (++iss_q == nq) {
+        iss_q = 0;
+        iss_qh += D;
+        iss_gh += D;
+        iss_rh += (long)a.Tq * 8;
+      }
+    };
+    auto mask_q0 = [&](int q0) {
+      return (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
+             (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
+    };
     auto mask_tile = [&](int t) {
       if (t >= ntiles) return false;
       const int q0 = tile_q0(t);
       return (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
              (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
     };
-    // Byte offset of block `blk` (32 rows): its tile's stage and its place in the tile.
-    // (one wave-uniform value, so that each read adds it to its lane offset in
-    // one instruction)
-    auto blk_off = [&](int blk) {
-      return (uint32_t)__builtin_amdgcn_readfirstlane(((blk / C::BPT) % C::NST) * TB + (blk % C::BPT) * BB);
-    };
+    // The byte offset of a 32-row block in the ring (its tile's stage and its
+    // place in the tile) is made one wave-uniform value, so that each read adds
+    // it to its lane offset in one instruction.
 
     // Row terms as one extra k-step (see the single-role kernel): the S wave
     // selects -LSE/scale, the dP wave -D.
@@ -197,12 +228,11 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
     const u32x4_t sel = hh != 0 ? u32x4_t{0, 0, 0, 0}
                         : role == 0 ? u32x4_t{one2, one1, 0, 0} : u32x4_t{0, 0, one2, one1};
 
-    // Row product of block blk: S (S wave) or dP (dP wave), row terms included.
-    auto row_product = [&](int blk) {
-      const uint32_t bo = blk_off(blk);
-      const int st = (blk / C::BPT) % C::NST;
-      const u32x4_t terms =
-          lds_read16((const uint16_t*)(smem + R_OFF + (st * C::BM + 32 * (blk % C::BPT) + l32) * 16));
+    // Row product of block `half` of the tile in stage `st`: S (S wave) or dP
+    // (dP wave), row terms included.
+    auto row_product_at = [&](int st, int half) {
+      const uint32_t bo = (uint32_t)__builtin_amdgcn_readfirstlane(st * TB + half * BB);
+      const u32x4_t terms = lds_read16((const uint16_t*)(smem + R_OFF + (st * C::BM + 32 * half + l32) * 16));
       u32x4_t ra[C::R];
 #pragma unroll
       for (int m = 0; m < C::R; ++m) ra[m] = lds_read16((const uint16_t*)(smem + row_off[m] + bo));
@@ -214,9 +244,11 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
       }
       return mfma_bf16(terms, sel, r);
     };
-    // Transposed product of block blk: acc += (dO or Q)^T x packed B operand.
-    auto tr_product = [&](int blk, const u32x4_t (&pk)[2]) {
-      const uint32_t bo = blk_off(blk);
+    auto row_product = [&](int blk) { return row_product_at((blk / C::BPT) % C::NST, blk % C::BPT); };
+    // Transposed product of block `half` of the tile in stage `st`:
+    // acc += (dO or Q)^T x packed B operand.
+    auto tr_product_at = [&](int st, int half, const u32x4_t (&pk)[2]) {
+      const uint32_t bo = (uint32_t)__builtin_amdgcn_readfirstlane(st * TB + half * BB);
       u32x2_t tra[C::R][2];
       auto rd = [&](int m, int slot) {
         const int u = m / C::DB, db = m % C::DB;
@@ -233,11 +265,19 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
         if (m + C::R < C::KS) rd(m + C::R, slot);
       }
     };
+    auto tr_product = [&](int blk, const u32x4_t (&pk)[2]) {
+      tr_product_at((blk / C::BPT) % C::NST, blk % C::BPT, pk);
+    };
     auto pack8 = [](const float* v) {
       return u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
     };
 
-    for (int t = 0; t < C::NST - 1 && t < ntiles; ++t) issue(t);
+    for (int t = 0; t < C::NST - 1 && t < ntiles; ++t) {
+      if constexpr (TWO)
+        issue_next();
+      else
+        issue(t);
+    }
     wait_vmem();
     __syncthreads();
     const int nb = C::BPT * ntiles;  // 32-row blocks
@@ -272,12 +312,13 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
     if (role == 0) {
       // P of block blk: exp2 of the row product, masked, packed, handed over.
       u32x4_t pk[2];
-      auto softmax = [&](int blk, const f32x16_t& s) {
+      // P of block blk of the tile at query row qt0 (masked when msk).
+      auto softmax_at = [&](int blk, const f32x16_t& s, bool msk, int qt0) {
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(s[r] * c);
-        if (mask_tile(blk / C::BPT)) {
-          const int q0 = tile_q0(blk / C::BPT) + 32 * (blk % C::BPT);
+        if (msk) {
+          const int q0 = qt0 + 32 * (blk % C::BPT);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = q0 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -292,35 +333,53 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
         lds_write16((uint16_t*)(smem + xo), pk[0]);
         lds_write16((uint16_t*)(smem + xo + 1024), pk[1]);
       };
+      auto softmax = [&](int blk, const f32x16_t& s) {
+        const int t = blk / C::BPT;
+        softmax_at(blk, s, mask_tile(t), t < ntiles ? tile_q0(t) : 0);
+      };
       if constexpr (TWO) {
         // Step j: the transposed products of tile j's blocks 2j and 2j + 1
         // (their P from the previous step) and the row products and softmax of
         // tile j + 1's blocks, one block after the other, then one barrier.
         u32x4_t pa[2], pb[2];
-        softmax(0, row_product(0));
+        // Softmax walk: query tile of the tile whose P is formed next.
+        int sm_q = 0;
+        bool msk = mask_q0(qt_begin * C::BM);
+        int sq0 = qt_begin * C::BM;
+        auto sm_advance = [&](int t_next) {
+          if (++sm_q == nq) sm_q = 0;
+          sq0 = (qt_begin + sm_q) * C::BM;
+          msk = t_next < ntiles && mask_q0(sq0);
+        };
+        softmax_at(0, row_product_at(0, 0), msk, sq0);
         pa[0] = pk[0];
         pa[1] = pk[1];
-        softmax(1, row_product(1));
+        softmax_at(1, row_product_at(0, 1), msk, sq0);
         pb[0] = pk[0];
         pb[1] = pk[1];
+        sm_advance(1);
         __syncthreads();
+        int st_j = 0, st_n = 1 % C::NST;  // stages of tiles j and j + 1
         for (int j = 0; j < ntiles; ++j) {
-          if (j + 2 < ntiles) issue(j + 2);
+          if (j + 2 < ntiles) issue_next();
           // The S wave issues its row product at raised priority: its
           // softmax, and through P the partner's next step, wait on it.
           __builtin_amdgcn_s_setprio(1);
-          f32x16_t s = row_product(2 * j + 2);
+          f32x16_t s = row_product_at(st_n, 0);
           __builtin_amdgcn_s_setprio(0);
-          tr_product(2 * j, pa);
-          softmax(2 * j + 2, s);
+          tr_product_at(st_j, 0, pa);
+          softmax_at(2 * j + 2, s, msk, sq0);
           pa[0] = pk[0];
           pa[1] = pk[1];
           __builtin_amdgcn_sched_barrier(0);  // one block's state live at a time
-          s = row_product(2 * j + 3);
-          tr_product(2 * j + 1, pb);
-          softmax(2 * j + 3, s);
+          s = row_product_at(st_n, 1);
+          tr_product_at(st_j, 1, pb);
+          softmax_at(2 * j + 3, s, msk, sq0);
           pb[0] = pk[0];
           pb[1] = pk[1];
+          sm_advance(j + 2);
+          st_j = st_n;
+          st_n = st_n + 1 == C::NST ? 0 : st_n + 1;
           wait_vmem();  // tile j + 2 (issued above) is read from the next step on
           __syncthreads();
         }
@@ -356,16 +415,17 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
       // carried blocks spilled), and the partner's vector work fills the wait
       // on each block's row product.
       __syncthreads();
+      int st_j = 0;  // stage of tile j
       for (int j = 0; j < ntiles; ++j) {
-        if (j + 2 < ntiles) issue(j + 2);
+        if (j + 2 < ntiles) issue_next();
         u32x4_t pk[2];
-        f32x16_t dp = row_product(2 * j);
-        ds_of(2 * j, dp, pk);
-        tr_product(2 * j, pk);
-        __builtin_amdgcn_sched_barrier(0);  // one block's state live at a time
-        dp = row_product(2 * j + 1);
-        ds_of(2 * j + 1, dp, pk);
-        tr_product(2 * j + 1, pk);
+        const f32x16_t dp0 = row_product_at(st_j, 0);
+        const f32x16_t dp1 = row_product_at(st_j, 1);
+        ds_of(2 * j, dp0, pk);
+        tr_product_at(st_j, 0, pk);
+        ds_of(2 * j + 1, dp1, pk);
+        tr_product_at(st_j, 1, pk);
+        st_j = st_j + 1 == C::NST ? 0 : st_j + 1;
         wait_vmem();  // tile j + 2 (issued above) is read from the next step on
         __syncthreads();
       }

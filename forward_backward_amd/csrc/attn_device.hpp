@@ -198,6 +198,65 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
       : "memory");
 }
 
+// Batched dma16_s: the ITERS copies of one tile (lane byte offsets voff[i],
+// LDS destinations lds + i * STEP) from base_a and, with TWO, the same copies
+// of a second tile from base_b to lds + AB + i * STEP, in one inline-asm
+// block, so that M0 is saved and restored once per batch and each further
+// destination is one scalar add of an immediate. lds must be wave-uniform.
+#define ATTN_DMA_AT(v, b) "s_nop 0\n\tglobal_load_lds_dwordx4 %[" v "], %[" b "]\n\t"
+#define ATTN_DMA_STEP(d) "s_add_u32 m0, m0, %[" d "]\n\t"
+template <int ITERS, int STEP, bool TWO, int AB = 0>
+__device__ __forceinline__ void dma16_batch(const void* base_a, const void* base_b, const uint32_t (&voff)[ITERS],
+                                            uint32_t lds) {
+  static_assert(ITERS == 2 || ITERS == 4, "two or four copies per tile");
+  auto uniform = [](const void* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32)));
+    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  const void* sa = uniform(base_a);
+  const uint32_t l0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+  uint32_t saved;
+  if constexpr (ITERS == 2 && !TWO) {
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [a] "s"(sa), [l0] "s"(l0), [st] "n"(STEP)
+                 : "memory");
+  } else if constexpr (ITERS == 2 && TWO) {
+    const void* sb = uniform(base_b);
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") ATTN_DMA_STEP("ab") ATTN_DMA_AT("v0", "b") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "b") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [a] "s"(sa), [b] "s"(sb), [l0] "s"(l0), [st] "n"(STEP),
+                   [ab] "n"(AB - STEP)
+                 : "memory");
+  } else if constexpr (ITERS == 4 && !TWO) {
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") ATTN_DMA_STEP("st") ATTN_DMA_AT("v2", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v3", "a") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]), [a] "s"(sa),
+                   [l0] "s"(l0), [st] "n"(STEP)
+                 : "memory");
+  } else {
+    const void* sb = uniform(base_b);
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") ATTN_DMA_STEP("st") ATTN_DMA_AT("v2", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v3", "a") ATTN_DMA_STEP("ab") ATTN_DMA_AT("v0", "b") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "b") ATTN_DMA_STEP("st") ATTN_DMA_AT("v2", "b") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v3", "b") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]), [a] "s"(sa),
+                   [b] "s"(sb), [l0] "s"(l0), [st] "n"(STEP), [ab] "n"(AB - 3 * STEP)
+                 : "memory");
+  }
+}
+#undef ATTN_DMA_AT
+#undef ATTN_DMA_STEP
+
 // Precomputed form of dma_tile for full tiles (every row valid): the lane
 // offsets (row * rs + swizzled chunk) are fixed at set-up, so each tile costs
 // one uniform base pointer. Needs (ROWS - 1) * rs * 2 + 2 * D < 2^32 bytes.
@@ -229,6 +288,19 @@ struct TileCopy {
     const uint32_t l0 = lds_addr(tile) + lds_wave;
 #pragma unroll
     for (int i = 0; i < ITERS; ++i) dma16_s(base, voff[i], l0 + i * WAVES * 1024);
+  }
+
+  // Rows [r0, r0 + ROWS) of two matrices with the same row stride into two
+  // tiles `ab_bytes` apart in LDS (tile_b = tile_a + AB bytes), one batch.
+  template <int AB>
+  __device__ __forceinline__ void copy2(uint16_t* tile_a, const uint16_t* ga, const uint16_t* gb, long rs,
+                                        int r0) const {
+    const long off = (long)r0 * rs;
+    dma16_batch<ITERS, WAVES * 1024, true, AB>(ga + off, gb + off, voff, lds_addr(tile_a) + lds_wave);
+  }
+  // One tile, one batch.
+  __device__ __forceinline__ void copy1(uint16_t* tile, const uint16_t* g, long rs, int r0) const {
+    dma16_batch<ITERS, WAVES * 1024, false>(g + (long)r0 * rs, nullptr, voff, lds_addr(tile) + lds_wave);
   }
 
   // Same through the compiler builtin (see dma_tile's VISIBLE).
