@@ -402,8 +402,9 @@ def time_decode(case, calls, sets=4):
         _, ds = device_tensors(case, seed=s, with_do=False)
         caches.append((ds["k"], ds["v"]))
     q, kv = d0["q"], d0["kv_lens"]
+    ws = attn.decode_workspace(q, caches[0][0])  # one workspace for every call
     for i in range(4):
-        attn.decode(q, *caches[i % sets], kv_lens=kv, scale=case.scale)
+        attn.decode(q, *caches[i % sets], kv_lens=kv, scale=case.scale, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -416,11 +417,11 @@ def time_decode(case, calls, sets=4):
 
     def eager():
         for i in range(calls):
-            attn.decode(q, *caches[i % sets], kv_lens=kv, scale=case.scale)
+            attn.decode(q, *caches[i % sets], kv_lens=kv, scale=case.scale, workspace=ws)
 
     def same():
         for i in range(calls):
-            attn.decode(q, *caches[0], kv_lens=kv, scale=case.scale)
+            attn.decode(q, *caches[0], kv_lens=kv, scale=case.scale, workspace=ws)
 
     cold = timed(eager)
     warm = timed(same)
@@ -698,13 +699,14 @@ def decode_suite(calls):
         q = device_normal((case.B, case.Tq, case.Hq, case.D), 1)
         caches = [(device_normal((case.B, case.Tkv, case.Hkv, case.D), 2 + 2 * i),
                    device_normal((case.B, case.Tkv, case.Hkv, case.D), 3 + 2 * i)) for i in range(sets)]
+        ws = attn.decode_workspace(q, caches[0][0])
         for i in range(2):
-            attn.decode(q, *caches[i % sets], scale=case.scale)
+            attn.decode(q, *caches[i % sets], scale=case.scale, workspace=ws)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(calls):
-            attn.decode(q, *caches[i % sets], scale=case.scale)
+            attn.decode(q, *caches[i % sets], scale=case.scale, workspace=ws)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / calls * 1e3

@@ -247,16 +247,27 @@ def bwd_dq(q, k, v, lse, do, ws, dq, scale=None, causal=False, kv_lens=None, win
                              nbytes, _stream()))
 
 
-def decode(q, k_cache, v_cache, kv_lens=None, scale=None, num_splits=0, want_lse=True):
-    """Split-KV decode: O [B,Tq,Hq,D] bf16 and LSE fp32 [B,Hq,Tq] (or None)."""
+def decode_workspace(q, k_cache, num_splits=0):
+    """A device workspace for attn_decode on this problem, reusable by later
+    calls of the same or a smaller problem (not by overlapping calls)."""
+    p = _params_for(q, k_cache, None, False, None)
+    need = lib().attn_decode_workspace_size(ctypes.byref(p), num_splits)
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+
+
+def decode(q, k_cache, v_cache, kv_lens=None, scale=None, num_splits=0, want_lse=True, workspace=None):
+    """Split-KV decode: O [B,Tq,Hq,D] bf16 and LSE fp32 [B,Hq,Tq] (or None).
+    ``workspace``: one from decode_workspace; without it one is allocated
+    for the call."""
     p = _params_for(q, k_cache, scale, False, kv_lens)
     _like("v_cache", v_cache, k_cache.shape, k_cache.dtype, q.device)
     o = torch.empty_like(q)
     lse_t = torch.empty(_lse_shape(p), dtype=torch.float32, device=q.device) if want_lse else None
     need = lib().attn_decode_workspace_size(ctypes.byref(p), num_splits)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nbytes = _workspace(ws, need, q.device)
     _check(lib().attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse_t),
-                             num_splits, _ptr(ws), ws.numel(), _stream()))
+                             num_splits, _ptr(ws), nbytes, _stream()))
     return o, lse_t
 
 

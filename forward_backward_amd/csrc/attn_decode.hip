@@ -199,12 +199,32 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   const uint16_t* kb = (const uint16_t*)a.k + ((long)b * a.Tkv * a.Hkv + kh) * D;
   const uint16_t* vb = (const uint16_t*)a.v + ((long)b * a.Tkv * a.Hkv + kh) * D;
 
+  // Q of the 64 packed rows goes to the ring's last stage (free until the
+  // loop's first copy) ahead of the first tiles, so that it has landed with
+  // tile 0 (through registers it would have waited for every copy issued
+  // before it); rows past the packed rows re-read the last one (never stored).
+  uint16_t* const q_lds = ring + (C::NST - 1) * 2 * C::TILE;
+  static_assert(C::ROWS * D * 2 <= 2 * C::TILE * 2, "Q fits in one stage");
+  {
+    constexpr int QB = C::ROWS * D * 2 / 1024;  // 1 KiB blocks of Q
+#pragma unroll
+    for (int i = 0; i < QB / 4; ++i) {
+      const int blk = 4 * i + wave;
+      const int off = blk * 1024 + lane * 16;    // byte offset in the [ROWS][D] tile
+      const int row = off / (2 * D);
+      int p = rbi * C::ROWS + row;
+      p = p < R ? p : R - 1;
+      const uint16_t* src =
+          (const uint16_t*)a.q + (((long)b * a.Tq + p / G) * a.Hq + kh * G + p % G) * D + (off % (2 * D)) / 2;
+      dma16(src, lds_addr(q_lds) + blk * 1024);
+    }
+  }
+
   const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
   auto issue = [&](int t) {
     uint16_t* st = ring + ((t - t_begin) % C::NST) * 2 * C::TILE;
     if ((t + 1) * C::BN <= kvlim) {
-      kvcopy.copy(st, kb, krs, t * C::BN);
-      kvcopy.copy(st + C::TILE, vb, krs, t * C::BN);
+      kvcopy.template copy2<C::TILE * 2>(st, kb, vb, krs, t * C::BN);
     } else {
       dma_tile<D, C::BN, C::THREADS>(st, kb, krs, t * C::BN, kvlim, tid);
       dma_tile<D, C::BN, C::THREADS>(st + C::TILE, vb, krs, t * C::BN, kvlim, tid);
@@ -218,19 +238,17 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
 
   const int prow = rbi * C::ROWS + 32 * rb + l32;  // packed row of this lane
   const bool row_ok = prow < R;
+  // Q has landed once tile 0 has (or every copy, without tiles); the second
+  // barrier keeps the last stage from being refilled before all waves read it.
+  if (ntiles > 0)
+    wait_tile<C::NST - 2, C::COPIES>(ntiles - 1);
+  else
+    wait_vmem();
+  __syncthreads();
   u32x4_t qf[C::KS];
-  {
-    const int i = row_ok ? prow / G : 0;
-    const int g = row_ok ? prow % G : 0;
-    const uint16_t* qp = (const uint16_t*)a.q + (((long)b * a.Tq + i) * a.Hq + kh * G + g) * D;
 #pragma unroll
-    for (int t = 0; t < C::KS; ++t) qf[t] = row_ok ? gload16(qp + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
-    // Take Q here: the compiler cannot see the ring copies, and a first use
-    // of Q inside the loop would make it wait for all loads (the copies
-    // included) on every iteration.
-#pragma unroll
-    for (int t = 0; t < C::KS; ++t) asm volatile("" ::"v"(qf[t]));
-  }
+  for (int t = 0; t < C::KS; ++t) qf[t] = lds_read16(q_lds + (32 * rb + l32) * D + 16 * t + 8 * hh);
+  __syncthreads();
 
   f32x16_t o[C::DB];
 #pragma unroll

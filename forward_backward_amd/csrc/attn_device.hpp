@@ -208,7 +208,16 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
 template <int ITERS, int STEP, bool TWO, int AB = 0>
 __device__ __forceinline__ void dma16_batch(const void* base_a, const void* base_b, const uint32_t (&voff)[ITERS],
                                             uint32_t lds) {
-  static_assert(ITERS == 2 || ITERS == 4, "two or four copies per tile");
+  if constexpr (ITERS != 2 && ITERS != 4) {
+    // Other counts (head_dim 32 and 256 tiles of some kernels): one copy at a time.
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) dma16_s(base_a, voff[i], lds + i * STEP);
+    if constexpr (TWO) {
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i) dma16_s(base_b, voff[i], lds + AB + i * STEP);
+    }
+    return;
+  }
   auto uniform = [](const void* p) {
     const uint64_t u = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
@@ -241,7 +250,7 @@ __device__ __forceinline__ void dma16_batch(const void* base_a, const void* base
                  : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]), [a] "s"(sa),
                    [l0] "s"(l0), [st] "n"(STEP)
                  : "memory");
-  } else {
+  } else if constexpr (ITERS == 4 && TWO) {
     const void* sb = uniform(base_b);
     asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
                  ATTN_DMA_AT("v1", "a") ATTN_DMA_STEP("st") ATTN_DMA_AT("v2", "a") ATTN_DMA_STEP("st")

@@ -146,8 +146,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_bf16_kernel(BwdArgs a) {
       uint16_t* qs = q_st + st * C::TILE;
       uint16_t* gs = g_st + st * C::TILE;
       if (q0 + C::BM <= a.Tq) {
-        qcopy.copy(qs, (const uint16_t*)a.q + hoff, qrs, q0);
-        qcopy.copy(gs, (const uint16_t*)a.dout + hoff, qrs, q0);
+        qcopy.template copy2<G_OFF - Q_OFF>(qs, (const uint16_t*)a.q + hoff, (const uint16_t*)a.dout + hoff, qrs, q0);
       } else {
         dma_tile<D, C::BM, C::THREADS>(qs, (const uint16_t*)a.q + hoff, qrs, q0, a.Tq, tid);
         dma_tile<D, C::BM, C::THREADS>(gs, (const uint16_t*)a.dout + hoff, qrs, q0, a.Tq, tid);

@@ -381,6 +381,7 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     uint16_t* ks = tiles + st * 2 * C::TILE;
     const int k0 = (j0 + it) * C::BN;
     if (k0 + C::BN <= kv_end) {
+      // One copy at a time here: one batch for both tiles measured 1% slower.
       kvcopy.copy(ks, kb, krs, k0);
       kvcopy.copy(ks + C::TILE, vb, krs, k0);
     } else {

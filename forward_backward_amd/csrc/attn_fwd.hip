@@ -88,14 +88,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   auto issue_k = [&](int j, uint16_t* dst) {
     const int k0 = (j0 + j) * C::BN;
     if (k0 + C::BN <= kv_end)
-      kvcopy.copy(dst, kb, krs, k0);
+      kvcopy.copy1(dst, kb, krs, k0);
     else
       dma_tile<D, C::BN, C::THREADS>(dst, kb, krs, k0, kv_end, tid);
   };
   auto issue_v = [&](int j, uint16_t* dst) {
     const int k0 = (j0 + j) * C::BN;
     if (k0 + C::BN <= kv_end)
-      kvcopy.copy(dst, vb, krs, k0);
+      kvcopy.copy1(dst, vb, krs, k0);
     else
       dma_tile<D, C::BN, C::THREADS>(dst, vb, krs, k0, kv_end, tid);
   };

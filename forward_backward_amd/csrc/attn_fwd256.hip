@@ -84,8 +84,7 @@ __global__ __launch_bounds__(FwdPairCfg<D>::THREADS) void attn_fwd_pair_kernel(F
     char* st = smem + (j % C::NST) * 2 * TB;
     const int k0 = (j0 + j) * C::BN;
     if (k0 + C::BN <= kv_end) {
-      kvcopy.copy((uint16_t*)st, kb, krs, k0);
-      kvcopy.copy((uint16_t*)(st + TB), vb, krs, k0);
+      kvcopy.template copy2<TB>((uint16_t*)st, kb, vb, krs, k0);
     } else {
       dma_tile<D, C::BN, C::THREADS>((uint16_t*)st, kb, krs, k0, kv_end, tid);
       dma_tile<D, C::BN, C::THREADS>((uint16_t*)(st + TB), vb, krs, k0, kv_end, tid);

@@ -38,7 +38,8 @@
  *     to [0, Tkv] by the kernels (the host cannot read it without a sync).
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
  *     asynchronous on it. The library never allocates, frees or
- *     synchronises, holds no state and is safe to call from several threads.
+ *     synchronises and is safe to call from several threads; its only state
+ *     is the per-device address of attn_decode_noalloc's static scratch.
  *   - Argument errors are reported before anything is launched: the call
  *     returns a status and attn_last_error() (thread-local) describes it.
  *     The pages' own rule is to reject what cannot be computed exactly

@@ -253,7 +253,7 @@ def test_workspace_errors_report_sizes_above_2_gib():
     assert need == 6 * 1024 * 8 * 65536 * 4 > 2**33
     assert L.attn_bwd(ctypes.byref(p), *([FAKE] * 9), FAKE, 1, None) == attn.ATTN_ERR_WORKSPACE
     assert f"{need} bytes needed, 1 given".encode() in L.attn_last_error()
-    d = P(B=65536, Tq=1, Tkv=1024, Hq=32, Hkv=8)
+    d = P(B=32768, Tq=1, Tkv=1024, Hq=32, Hkv=8)  # 262144 segments, the most the counters take
     wneed = L.attn_decode_workspace_size(ctypes.byref(d), 0)
     assert wneed > 2**32
     assert L.attn_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, wneed - 16, None) == \
@@ -278,3 +278,4 @@ def test_noalloc_decode_rejects_oversized_calls_before_touching_a_device():
     assert L.attn_decode_noalloc(ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, None, -1, None) == attn.ATTN_ERR_INVALID
     assert L.attn_decode_noalloc(ctypes.byref(P(causal=True)), FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
         attn.ATTN_ERR_INVALID
+

@@ -109,3 +109,39 @@ def test_decode_caches_past_2_31_elements():
     print(f"    o rel err {err:.3e}", flush=True)
     assert err <= TOL["bf16"], f"O rel err {err:.3e}"
     check_lse(to_host64(lse[:small.B]), rlse)
+
+
+@pytest.mark.parametrize("case", [
+    Case("dec_all_lengths_zero", 3, 4, 500, 8, 2, 128, kv_lens=(0, 0, 0), workload_id=210, decode=True),
+    Case("dec_empty_cache", 2, 3, 0, 4, 1, 64, workload_id=211, decode=True),
+], ids=lambda c: c.name)
+def test_decode_without_valid_keys_writes_zeros(case):
+    """Segments with no valid key get no key range; the combine writes O = 0
+    and LSE = -inf for every one of their rows."""
+    import torch
+    host, dev, _ = device_inputs(case, with_do=False)
+    print(f"[decode empty] {case.name}", flush=True)
+    o, lse = run_decode(case, dev)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0.0)
+    assert torch.all(torch.isneginf(lse))
+
+
+def test_decode_workspace_reuse():
+    """One workspace serves calls of several shapes and split budgets: each
+    result equals a call with a fresh workspace bit for bit."""
+    import torch
+    from forward_backward_amd import attn
+    big = workload_cases(4)[0]
+    host, dev, _ = device_inputs(big, with_do=False)
+    ws = attn.decode_workspace(dev["q"], dev["k"], num_splits=1000)
+    runs = [(big, 0), (SMALL[1], 1000), (SMALL[5], 0), (big, 7), (SMALL[6], 2), (big, 0)]
+    for case, splits in runs:
+        print(f"[decode workspace reuse] {case.name} splits={splits}", flush=True)
+        _, d, _ = device_inputs(case, with_do=False)
+        o, lse = attn.decode(d["q"], d["k"], d["v"], kv_lens=d["kv_lens"], scale=case.scale, num_splits=splits,
+                             workspace=ws)
+        o2, lse2 = attn.decode(d["q"], d["k"], d["v"], kv_lens=d["kv_lens"], scale=case.scale, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
