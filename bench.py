@@ -52,7 +52,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the causal and decode legs")
     ap.add_argument("--decode-calls", type=int, default=200)
@@ -70,6 +70,10 @@ def parse_args():
     ap.add_argument("--summarize-fp32", metavar="STATS_DIR",
                     help="turn a rocprofv3 kernel trace of the fp32 suite into profiles/fp32_grid_kernel_stats.md "
                          "and exit (no GPU use); --profile-command records the command")
+    ap.add_argument("--summarize-suites", metavar="BENCH_LOG",
+                    help="turn the JSON line of a `bench.py --suites` run (the last line starting with '{' in "
+                         "BENCH_LOG) into profiles/suites_and_legs.md and exit (no GPU use); --profile-command "
+                         "records the command")
     ap.add_argument("--profile-command", default="", help="kernel-trace command recorded in the summaries")
     ap.add_argument("--counter-command", default="", help="counter-pass command recorded in the summaries")
     ap.add_argument("--mfma-dir", default="", help="with --summarize: rocprofv3 output of a pass with "
@@ -344,8 +348,23 @@ def device_tensors(case, seed=0, with_do=True):
     return host, dev
 
 
-def time_train_steps(case, steps, warmup):
-    """K timed fwd+bwd steps; returns (ms_per_step, {kernel: avg_ms})."""
+def quartiles(xs):
+    """Median, first and third quartile (linear interpolation), min and max."""
+    v = sorted(xs)
+    n = len(v)
+
+    def q(f):
+        x = f * (n - 1)
+        i = int(x)
+        return v[i] if i + 1 >= n else v[i] + (x - i) * (v[i + 1] - v[i])
+
+    return {"median": round(q(0.5), 4), "q1": round(q(0.25), 4), "q3": round(q(0.75), 4),
+            "min": round(v[0], 4), "max": round(v[-1], 4)}
+
+
+def time_train_steps(case, steps, warmup, spread=False):
+    """K timed fwd+bwd steps; returns (ms_per_step, {kernel: avg_ms}) and, with
+    spread, the median and quartiles of the K per-step and per-kernel times."""
     import torch
     from forward_backward_amd import attn
 
@@ -382,7 +401,11 @@ def time_train_steps(case, steps, warmup):
     per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
     if not torch.isfinite(dq.float()).all() or not torch.isfinite(o.float()).all():
         raise RuntimeError("non-finite outputs in the benchmark step")
-    return total / steps, per
+    if not spread:
+        return total / steps, per
+    dist = {"step_ms": quartiles([e[0].elapsed_time(e[4]) for e in evs]),
+            "per_kernel_ms": {n: quartiles([e[j].elapsed_time(e[j + 1]) for e in evs]) for j, n in enumerate(names)}}
+    return total / steps, per, dist
 
 
 def time_decode(case, calls, sets=4):
@@ -425,6 +448,7 @@ def time_decode(case, calls, sets=4):
 
     cold = timed(eager)
     warm = timed(same)
+    mem = decode_memory(q, caches[0], kv, case.scale)
     # Outputs and workspaces allocated during capture live in the graph's
     # memory pool for as long as the graph object does.
     graph = torch.cuda.CUDAGraph()
@@ -437,7 +461,29 @@ def time_decode(case, calls, sets=4):
     torch.cuda.synchronize()
     replay = min(timed(graph.replay) for _ in range(3))
     del graph
-    return replay, cold, warm, [int(x) for x in host["kv_lens"]]
+    return replay, cold, warm, [int(x) for x in host["kv_lens"]], mem
+
+
+def decode_memory(q, cache, kv, scale):
+    """Workspace bytes, output bytes (O and LSE) and the device peak beyond the
+    inputs of one attn_decode call that allocates its own outputs and workspace."""
+    import ctypes
+    import torch
+    from forward_backward_amd import attn
+
+    B, Tq, Hq, D = q.shape
+    _, Tkv, Hkv, _ = cache[0].shape
+    p = attn.make_params(B, Tq, Tkv, Hq, Hkv, D)
+    ws = int(attn.lib().attn_decode_workspace_size(ctypes.byref(p), 0))
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o, lse = attn.decode(q, *cache, kv_lens=kv, scale=scale)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    out = o.numel() * o.element_size() + lse.numel() * lse.element_size()
+    return {"workspace_bytes": ws, "output_bytes": int(out), "device_peak_bytes": int(peak),
+            "device_peak": "beyond the resident inputs; torch's caching allocator rounds each block up"}
 
 
 def gemm_ceiling():
@@ -572,6 +618,117 @@ def headdim_sweep(steps):
     return {"shape": "bf16 B4 H8 T4096 non-causal, fwd+bwd", "rows": rows}
 
 
+def _fwd_ms(q, k, v, kw, n):
+    import torch
+    from forward_backward_amd import attn
+    for _ in range(2):
+        attn.fwd(q, k, v, **kw)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        attn.fwd(q, k, v, **kw)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _step_ms(q, k, v, do, kw, n):
+    import torch
+    from forward_backward_amd import attn
+
+    def step():
+        o, lse = attn.fwd(q, k, v, **kw)
+        return attn.bwd(q, k, v, o, lse, do, **kw)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def short_and_kvlen_legs(n):
+    """The head_dim-64 grid's lengths up to 1024 (fwd and fwd+bwd, causal and not) and the KV-length
+    workload (fwd+bwd, TFLOP/s over the nominal FLOPs and over the keys inside the lengths)."""
+    import torch
+    from forward_backward_amd.inputs import make_inputs, workload_cases
+    from forward_backward_amd.metrics import attention_flops, effective_flops
+
+    rows = []
+    for case in workload_cases(1):
+        if case.Tq > 1024:
+            continue
+        q = device_normal((case.B, case.Tq, case.Hq, case.D), 1)
+        k = device_normal((case.B, case.Tkv, case.Hkv, case.D), 2)
+        v = device_normal((case.B, case.Tkv, case.Hkv, case.D), 3)
+        do = device_normal((case.B, case.Tq, case.Hq, case.D), 4)
+        kw = dict(scale=case.scale, causal=case.causal)
+        f_ms, fb_ms = _fwd_ms(q, k, v, kw, n), _step_ms(q, k, v, do, kw, n)
+        ffl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, case.causal, "fwd")
+        fbfl = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, case.causal, "fwd_bwd")
+        rows.append({"case": case.name, "fwd_us": round(f_ms * 1e3, 2), "fwd_tflops": round(ffl / (f_ms * 1e-3) / 1e12, 1),
+                     "fwd_bwd_us": round(fb_ms * 1e3, 2),
+                     "fwd_bwd_tflops": round(fbfl / (fb_ms * 1e-3) / 1e12, 1)})
+        log(f"  {case.name}: fwd {f_ms * 1e3:.1f} us, fwd+bwd {fb_ms * 1e3:.1f} us")
+        del q, k, v, do
+    (case,) = workload_cases(3)
+    lens = [int(x) for x in make_inputs(case, with_do=False)["kv_lens"]]
+    q = device_normal((case.B, case.Tq, case.Hq, case.D), 1)
+    k = device_normal((case.B, case.Tkv, case.Hkv, case.D), 2)
+    v = device_normal((case.B, case.Tkv, case.Hkv, case.D), 3)
+    do = device_normal((case.B, case.Tq, case.Hq, case.D), 4)
+    kw = dict(scale=case.scale, causal=False, kv_lens=torch.tensor(lens, dtype=torch.int32, device=q.device))
+    fb_ms = _step_ms(q, k, v, do, kw, n)
+    nominal = attention_flops(case.B, case.Hq, case.Tq, case.Tkv, case.D, False, "fwd_bwd")
+    eff = effective_flops(case.Hq, case.Tq, lens, case.D, "fwd_bwd")
+    kvlen = {"workload": case.name, "kv_lens": lens, "fwd_bwd_ms": round(fb_ms, 4),
+             "nominal_tflops": round(nominal / (fb_ms * 1e-3) / 1e12, 1),
+             "effective_tflops": round(eff / (fb_ms * 1e-3) / 1e12, 1),
+             "effective_frac": round(eff / (fb_ms * 1e-3) / 1e12 / 2516.6, 4)}
+    log(f"  {case.name}: fwd+bwd {fb_ms:.3f} ms, {kvlen['effective_tflops']} TFLOP/s effective")
+    return {"shape": "bf16 B4 H8 d64, T <= 1024", "rows": rows}, kvlen
+
+
+def memory_suite():
+    """The pages' memory figures ("Attention performance", section "Memory"): the device peak of one
+    fwd+bwd call (bf16, head_dim 64, batch 4, 8 heads, non-causal) by length, up to 65536 (the length
+    the pages' search stopped at), and the bytes kept for the backward (O and LSE; batch 2, 8 heads,
+    head_dim 64)."""
+    import torch
+    from forward_backward_amd import attn
+
+    peak_rows, res_rows = [], []
+    for T in (1024, 4096, 16384, 65536):
+        q = device_normal((4, T, 8, 64), 1)
+        k = device_normal((4, T, 8, 64), 2)
+        v = device_normal((4, T, 8, 64), 3)
+        do = device_normal((4, T, 8, 64), 4)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        o, lse = attn.fwd(q, k, v)
+        dq, dk, dv = attn.bwd(q, k, v, o, lse, do)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        peak_rows.append({"T": T, "ran": True, "device_peak_mb": round(peak / 2**20, 2),
+                          "inputs_mb": round(4 * q.numel() * 2 / 2**20, 1)})
+        log(f"  fwd+bwd B4 H8 d64 T{T}: peak {peak / 2**20:.1f} MB beyond the inputs")
+        del q, k, v, do, o, lse, dq, dk, dv
+        q = device_normal((2, T, 8, 64), 1)
+        k = device_normal((2, T, 8, 64), 2)
+        o, lse = attn.fwd(q, k, k)
+        res = o.numel() * o.element_size() + lse.numel() * lse.element_size()
+        res_rows.append({"T": T, "residual_mb": round(res / 2**20, 3), "kept": "O (bf16) and LSE (fp32)"})
+        del q, k, o, lse
+    return {"device_peak": {"shape": "bf16 B4 H8 d64 non-causal, one fwd+bwd call, beyond q/k/v/dO",
+                            "largest_T_run": 65536, "rows": peak_rows},
+            "residuals": {"shape": "bf16 B2 H8 d64, bytes kept for the backward", "rows": res_rows}}
+
+
 def config_grid(steps):
     """The pages' head_dim-64 grid (bf16 B4 H8 d64, T in {512, 1024, 2048, 600, 1500, 3000}, causal and
     not; fwd and fwd+bwd) and the KV-length case (bf16 B4 H8 d128 T4096, kv_len {1, 777, 2500, 4096},
@@ -704,19 +861,31 @@ def decode_suite(calls):
             attn.decode(q, *caches[i % sets], scale=case.scale, workspace=ws)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(calls):
-            attn.decode(q, *caches[i % sets], scale=case.scale, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / calls * 1e3
+        rounds = []
+        for _ in range(3):  # median of three rounds, as the pages report
+            e0.record()
+            for i in range(calls):
+                attn.decode(q, *caches[i % sets], scale=case.scale, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            rounds.append(e0.elapsed_time(e1) / calls * 1e3)
+        us = sorted(rounds)[1]
+        del ws
+        mem = decode_memory(q, caches[0], None, case.scale)
         nbytes = decode_bytes(case.B, case.Tq, case.Hq, case.Hkv, case.D, [case.Tkv] * case.B)
         row = {"B": case.B, "keys": case.Tkv, "Hkv": case.Hkv, "us_per_call": round(us, 2),
-               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes_per_call": nbytes, "cache_copies": sets}
+               "us_rounds": [round(r, 2) for r in rounds],
+               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes_per_call": nbytes, "cache_copies": sets,
+               "workspace_bytes": mem["workspace_bytes"], "output_bytes": mem["output_bytes"],
+               "device_peak_bytes": mem["device_peak_bytes"]}
         rows.append(row)
-        log(f"  decode B{case.B} keys {case.Tkv} Hkv{case.Hkv}: {us:.1f} us/call, {row['gbs']} GB/s")
+        log(f"  decode B{case.B} keys {case.Tkv} Hkv{case.Hkv}: {us:.1f} us/call, {row['gbs']} GB/s, workspace "
+            f"{row['workspace_bytes'] / 2**20:.2f} MiB, peak {row['device_peak_bytes'] / 2**20:.2f} MiB")
         del q, caches
-    return {"shape": "bf16 Tq=1 Hq32 d128, full caches, eager calls", "rows": rows}
+    return {"shape": "bf16 Tq=1 Hq32 d128, full caches, eager calls, median of three rounds",
+            "memory": "workspace_bytes: attn_decode_workspace_size; output_bytes: O and LSE; device_peak_bytes: "
+                      "one call that allocates its outputs and workspace, beyond the resident inputs",
+            "rows": rows}
 
 
 def cpu_baseline(case, seconds):
@@ -754,6 +923,110 @@ def cpu_baseline(case, seconds):
                   f"float64 NumPy, {t_used:.1f} s",
         "seconds": t_used,
     }
+
+
+def blas_info():
+    """The BLAS library NumPy runs on, and its thread count."""
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                return f"{p.get('internal_api')} {p.get('version')} ({os.path.basename(p.get('filepath', ''))})", \
+                    int(p.get("num_threads", 1))
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return "unknown", len(os.sched_getaffinity(0))
+
+
+def cpu_oracle_configs():
+    """The float64 oracle on every workload, forward and forward+backward timed separately, median of
+    three calls; the two small workloads also with one thread. Large workloads are timed on a sample
+    (one query head for the forward, one KV head with its query heads for the backward) and priced by
+    the FLOPs of that sample; the KV-length workload samples one KV head per batch (the lengths
+    differ), priced by the keys inside each length; decode runs whole. Sizes are chosen so that the
+    whole table takes well under a minute on 16 host threads."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from forward_backward_amd import inputs as I
+    from forward_backward_amd.inputs import workload_cases
+    from forward_backward_amd.metrics import attention_flops, effective_flops
+    import oracle
+
+    blas, threads = blas_info()
+
+    def med3(fn, reps=3):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2]
+
+    def sample_slices(case, host, groups):
+        out = []
+        G = case.Hq // case.Hkv
+        for b, kh in groups:
+            sl = lambda x, hs: I.to_float64(x[b:b + 1, :, hs], case.dtype)  # noqa: E731
+            lens = None if host["kv_lens"] is None else host["kv_lens"][b:b + 1]
+            out.append(dict(q1=sl(host["q"], slice(kh * G, kh * G + 1)), qg=sl(host["q"], slice(kh * G, (kh + 1) * G)),
+                            k=sl(host["k"], slice(kh, kh + 1)), v=sl(host["v"], slice(kh, kh + 1)),
+                            do=sl(host["do"], slice(kh * G, (kh + 1) * G)), lens=lens, G=G))
+        return out
+
+    def time_case(case, groups, single=False, reps=3):
+        host = I.make_inputs(case, seed=0)
+        sm = sample_slices(case, host, groups)
+
+        def fwd():
+            for x in sm:
+                oracle.attention_fwd(x["q1"], x["k"], x["v"], case.scale, case.causal, x["lens"], window=case.window)
+
+        def fwd_bwd():
+            for x in sm:
+                oracle.attention_fwd(x["qg"], x["k"], x["v"], case.scale, case.causal, x["lens"], window=case.window)
+                oracle.attention_bwd(x["qg"], x["k"], x["v"], x["do"], case.scale, case.causal, x["lens"],
+                                     window=case.window)
+
+        if case.kv_lens is not None or case.kv_len_range is not None:
+            lens = [int(host["kv_lens"][b]) for b, _ in groups]
+            f1 = effective_flops(1, case.Tq, lens, case.D, "fwd")
+            fg = effective_flops(sm[0]["G"], case.Tq, lens, case.D, "fwd_bwd")
+        else:
+            f1 = len(groups) * attention_flops(1, 1, case.Tq, case.Tkv, case.D, case.causal, "fwd")
+            fg = len(groups) * attention_flops(1, sm[0]["G"], case.Tq, case.Tkv, case.D, case.causal, "fwd_bwd")
+        # fwd+bwd first: it also warms the allocation of the score-sized arrays the forward then reuses.
+        fb = round(med3(fwd_bwd, reps) * 1e3, 3)
+        row = {"workload": case.name, "sample": f"{len(groups)} of {case.B * case.Hkv} (batch, KV head) groups",
+               "calls": reps, "fwd_ms": round(med3(fwd, reps) * 1e3, 3), "fwd_bwd_ms": fb}
+        row["fwd_gflops"] = round(f1 / (row["fwd_ms"] * 1e-3) / 1e9, 2)
+        row["fwd_bwd_gflops"] = round(fg / (row["fwd_bwd_ms"] * 1e-3) / 1e9, 2)
+        if single:
+            with threadpool_limits(limits=1, user_api="blas"):
+                row["fwd_ms_1thread"] = round(med3(fwd) * 1e3, 3)
+                row["fwd_bwd_ms_1thread"] = round(med3(fwd_bwd) * 1e3, 3)
+        return row
+
+    t_start = time.perf_counter()
+    rows = []
+    (c1,) = workload_cases(0)
+    rows.append(time_case(c1, [(0, h) for h in range(c1.Hkv)], single=True))
+    rows[-1]["sample"] = "whole workload"
+    for case in workload_cases(1):
+        rows.append(time_case(case, [(0, 0)], single=case.Tq <= 1024))
+    for case in workload_cases(2):
+        rows.append(time_case(case, [(0, 0)], reps=1))
+    (c4,) = workload_cases(3)
+    rows.append(time_case(c4, [(b, 0) for b in range(c4.B)], reps=1))
+    (c5,) = workload_cases(4)
+    host = I.make_inputs(c5, seed=0, with_do=False)
+    f64 = {n: I.to_float64(host[n], c5.dtype) for n in ("q", "k", "v")}
+    dec_ms = med3(lambda: oracle.attention_decode(f64["q"], f64["k"], f64["v"], c5.scale, host["kv_lens"])) * 1e3
+    fl = effective_flops(c5.Hq, c5.Tq, host["kv_lens"], c5.D, "fwd")
+    rows.append({"workload": c5.name, "sample": "whole workload", "fwd_ms": round(dec_ms, 3),
+                 "fwd_gflops": round(fl / (dec_ms * 1e-3) / 1e9, 2)})
+    log(f"  oracle per workload: {time.perf_counter() - t_start:.1f} s")
+    return {"blas": blas, "threads": threads,
+            "unit": "ms per call of the sample (median of `calls`); GFLOP/s of the sample", "rows": rows}
 
 
 STALL_COUNTERS = {
@@ -828,8 +1101,105 @@ def summarize_stalls(pmc_dirs, command, out_dir=""):
     log(f"wrote {path}")
 
 
+def summarize_suites(log_path, command, out_dir=""):
+    """Markdown tables of every leg and suite of one bench line."""
+    line = [x for x in open(log_path) if x.startswith("{")][-1]
+    d = json.loads(line)
+    L = ["# Every leg of one bench run: headline, causal, window, decode, short sequences, KV lengths, suites",
+         "", "One `bench.py` run on one MI355X (the JSON line it printed, in tables). Command:", "",
+         "```", command or "(not recorded)", "```", ""]
+    sp = d.get("timing_spread", {}).get("per_step_ms", {})
+    L += ["## Headline (bf16 B4 H8 d128 T8192, non-causal, fwd+bwd)", "",
+          f"- {d['value']} TFLOP/s over {d['steps']} timed steps ({d['ms_per_step']} ms per step, mean); "
+          f"per step median {sp.get('median')} ms, quartiles {sp.get('q1')} / {sp.get('q3')} ms",
+          f"- per kernel ms (mean): {d['per_kernel_ms']}",
+          f"- roofline of `{d['roofline']['kernel']}`: {d['roofline']['achieved']} TFLOP/s, "
+          f"{d['roofline']['frac']:.1%} of {d['roofline']['peak']}", ""]
+    if "causal" in d:
+        c = d["causal"]
+        L += [f"- causal: {c['ms_per_step']} ms, {c['tflops']} TFLOP/s; per kernel {c['per_kernel_ms']}"]
+    if "window" in d:
+        w = d["window"]
+        L += [f"- causal 1024-key window: {w['ms_per_step']} ms, {w['tflops_visible']} TFLOP/s over visible pairs"]
+    if "decode" in d:
+        x = d["decode"]
+        r = x["roofline"]
+        L += [f"- GQA decode (B4, 32 query heads over 8 KV heads, 16 queries, 16384-key caches, lengths "
+              f"{x['kv_lens']}): {x['us_per_call']} us per call in a graph ({r['achieved']} GB/s algorithmic, "
+              f"{r['frac']:.1%} of HBM; counter traffic {r.get('traffic')} B); eager {x['us_per_call_eager']} us; "
+              f"memory {x.get('memory')}"]
+    L.append("")
+    if "short_sequences" in d:
+        L += ["## Short sequences (bf16 B4 H8 d64)", "", "| case | fwd us | fwd TFLOP/s | fwd+bwd us | fwd+bwd TFLOP/s |",
+              "|---|---|---|---|---|"]
+        L += [f"| {r['case']} | {r['fwd_us']} | {r['fwd_tflops']} | {r['fwd_bwd_us']} | {r['fwd_bwd_tflops']} |"
+              for r in d["short_sequences"]["rows"]]
+        L.append("")
+    if "kv_len" in d:
+        x = d["kv_len"]
+        L += [f"KV-length workload ({x['workload']}, lengths {x['kv_lens']}): fwd+bwd {x['fwd_bwd_ms']} ms, "
+              f"{x['effective_tflops']} TFLOP/s over the keys inside the lengths ({x['nominal_tflops']} nominal).", ""]
+    if "gqa_suite" in d:
+        L += ["## GQA suite (bf16 B1, 32 query heads over 8 KV heads, d128, fwd+bwd)", "",
+              "| T | ms | TFLOP/s | peak MB | repeated K/V ms | repeated K/V peak MB |", "|---|---|---|---|---|---|"]
+        L += [f"| {r['T']} | {r['ms']} | {r['tflops']} | {r['peak_mb']} | {r['repeated_ms']} | {r['repeated_peak_mb']} |"
+              for r in d["gqa_suite"]["rows"]]
+        L.append("")
+    if "decode_suite" in d:
+        L += ["## Decode suite (bf16, one query, 32 query heads, d128, full caches; median of three rounds)", "",
+              "| B | keys | KV heads | us per call | GB/s | workspace MiB | output bytes | device peak MiB |",
+              "|---|---|---|---|---|---|---|---|"]
+        L += [f"| {r['B']} | {r['keys']} | {r['Hkv']} | {r['us_per_call']} | {r['gbs']} | "
+              f"{r['workspace_bytes'] / 2**20:.2f} | {r['output_bytes']} | {r['device_peak_bytes'] / 2**20:.2f} |"
+              for r in d["decode_suite"]["rows"]]
+        L.append("")
+    if "headdim_sweep" in d:
+        L += ["## head_dim sweep (bf16 B4 H8 T4096, fwd+bwd)", "", "| D | ms | TFLOP/s |", "|---|---|---|"]
+        L += [f"| {r['D']} | {r['ms']} | {r['tflops']} |" for r in d["headdim_sweep"]["rows"]]
+        L.append("")
+    if "config_grid" in d:
+        L += ["## head_dim-64 grid (bf16 B4 H8)", "", "| case | fwd ms | fwd TFLOP/s | fwd+bwd ms | fwd+bwd TFLOP/s |",
+              "|---|---|---|---|---|"]
+        L += [f"| {r['case']} | {r['fwd_ms']} | {r['fwd_tflops']} | {r['fwd_bwd_ms']} | {r['fwd_bwd_tflops']} |"
+              for r in d["config_grid"]["head_dim64_grid"]["rows"]]
+        L.append("")
+    if "memory" in d:
+        m = d["memory"]
+        L += ["## Memory", "", "| fwd+bwd bf16 B4 H8 d64, T | device peak MB beyond inputs | inputs MB |", "|---|---|---|"]
+        L += [f"| {r['T']} | {r['device_peak_mb']} | {r['inputs_mb']} |" for r in m["device_peak"]["rows"]]
+        L += ["", "| bytes kept for the backward, bf16 B2 H8 d64, T | MB (O and LSE) |", "|---|---|"]
+        L += [f"| {r['T']} | {r['residual_mb']} |" for r in m["residuals"]["rows"]]
+        L.append("")
+    if "fp32_suite" in d:
+        L += ["## fp32 grid (B4 H8)", "", "| case | fwd ms | fwd TFLOP/s | fwd+bwd ms | fwd+bwd TFLOP/s | of fp32 peak |",
+              "|---|---|---|---|---|---|"]
+        L += [f"| {r['case']} | {r['fwd_ms']} | {r['fwd_tflops']} | {r['fwd_bwd_ms']} | {r['fwd_bwd_tflops']} | "
+              f"{r['fwd_bwd_frac_fp32_peak']:.0%} |" for r in d["fp32_suite"]["rows"]]
+        L.append("")
+    if d.get("cpu_baseline"):
+        c = d["cpu_baseline"]
+        L += ["## CPU oracle (float64 NumPy on the host cores)", "",
+              f"Headline sample: {c['value'] * 1e3:.1f} GFLOP/s on {c['cores']} threads ({c['sample']}); BLAS "
+              f"{c.get('blas')}.", ""]
+        pw = c.get("per_workload")
+        if pw:
+            L += [f"Per workload ({pw['unit']}; {pw['threads']} BLAS threads):", "",
+                  "| workload | sample | calls | fwd ms | fwd+bwd ms | fwd ms, 1 thread | fwd+bwd ms, 1 thread |",
+                  "|---|---|---|---|---|---|---|"]
+            L += [f"| {r['workload']} | {r['sample']} | {r.get('calls', 3)} | {r.get('fwd_ms')} | {r.get('fwd_bwd_ms', '-')} | "
+                  f"{r.get('fwd_ms_1thread', '-')} | {r.get('fwd_bwd_ms_1thread', '-')} |" for r in pw["rows"]]
+            L.append("")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "suites_and_legs.md")
+    with open(path, "w") as f:
+        f.write("\n".join(L) + "\n")
+    print(f"wrote {path}")
+
+
 def main():
     args = parse_args()
+    if args.summarize_suites:
+        summarize_suites(args.summarize_suites, args.profile_command)
+        return
     if args.summarize_stalls:
         summarize_stalls(args.summarize_stalls, args.counter_command)
         return
@@ -870,9 +1240,15 @@ def main():
 
     full, causal = workload_cases(2)
     log(f"headline {full.name}: warmup {args.warmup}, steps {args.steps}")
-    ms, per = time_train_steps(full, args.steps, args.warmup)
+    ms, per, dist = time_train_steps(full, args.steps, args.warmup, spread=True)
     flops = attention_flops(full.B, full.Hq, full.Tq, full.Tkv, full.D, False, "fwd_bwd")
     tflops = flops / (ms * 1e-3) / 1e12
+    step_q = dist["step_ms"]
+    spread = {"per_step_ms": step_q,
+              "tflops_at": {k: round(flops / (step_q[v] * 1e-3) / 1e12, 2) for k, v in
+                            (("median", "median"), ("q1_time", "q1"), ("q3_time", "q3"))},
+              "per_kernel_ms": dist["per_kernel_ms"],
+              "note": "median and quartiles over the K timed steps (HIP events around each step and kernel)"}
     log(f"  {ms:.3f} ms/step, {tflops:.1f} TFLOP/s; per kernel ms: " +
         ", ".join(f"{k} {v:.3f}" for k, v in per.items()))
 
@@ -893,7 +1269,7 @@ def main():
         "flops_per_launch": kernel_flops[dom],
     }
 
-    extra = {}
+    extra = {"timing_spread": spread}
     if not args.no_extra:
         log(f"causal {causal.name}")
         cms, cper = time_train_steps(causal, args.steps, 1)
@@ -913,18 +1289,29 @@ def main():
                            "per_kernel_ms": {k: round(v, 4) for k, v in wper.items()}}
         log(f"  {wms:.3f} ms/step, {extra['window']['tflops_visible']} TFLOP/s over visible pairs")
         (dec,) = workload_cases(4)
-        graph_ms, cold, warm, lens = time_decode(dec, args.decode_calls)
+        graph_ms, cold, warm, lens, dmem = time_decode(dec, args.decode_calls)
         nbytes = decode_bytes(dec.B, dec.Tq, dec.Hq, dec.Hkv, dec.D, lens)
         gbs = nbytes / (graph_ms * 1e-3) / 1e9
+        counted = [stored_traffic(KERNEL_SYMBOLS[k]) for k in ("decode_split", "decode_combine")]
+        counter_bytes = sum(counted) if all(c is not None for c in counted) else None
         extra["decode"] = {
             "workload": dec.name, "kv_lens": lens, "us_per_call": round(graph_ms * 1e3, 2),
             "timing": "HIP graph of captured calls, 4 K/V caches in rotation",
             "us_per_call_eager": round(cold * 1e3, 2), "us_per_call_same_cache_eager": round(warm * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": nbytes},
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_call": nbytes,
+                         "traffic": counter_bytes,
+                         "counter_gbs": None if counter_bytes is None else
+                         round(counter_bytes / (graph_ms * 1e-3) / 1e9, 1),
+                         "traffic_note": "FETCH_SIZE + WRITE_SIZE of the split and combine kernels per call, "
+                                         "scaled by a plain copy (profiles/hbm_traffic.json); null when the "
+                                         "kernel sources changed since the counters were taken"},
+            "memory": dmem,
         }
         log(f"decode {graph_ms * 1e3:.1f} us/call in a graph ({gbs:.0f} GB/s); eager {cold * 1e3:.1f} us, "
             f"same cache {warm * 1e3:.1f} us")
+        log("short sequences and the KV-length workload")
+        extra["short_sequences"], extra["kv_len"] = short_and_kvlen_legs(max(args.steps, 20))
 
     if args.gemm_ceiling:
         log("bf16 GEMM through torch (hipBLASLt)")
@@ -938,6 +1325,8 @@ def main():
         extra["headdim_sweep"] = headdim_sweep(max(2, min(args.steps, 5)))
         log("head_dim 64 grid and KV-length case")
         extra["config_grid"] = config_grid(max(2, min(args.steps, 5)))
+        log("memory")
+        extra["memory"] = memory_suite()
     if args.suites or args.fp32_suite:
         log("fp32 suite")
         extra["fp32_suite"] = fp32_suite(max(2, min(args.steps, 5)))
@@ -947,6 +1336,8 @@ def main():
         log("cpu baseline (float64 oracle)")
         cpu = cpu_baseline(full, args.cpu_seconds)
         log(f"  {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
+        cpu["blas"] = blas_info()[0]
+        cpu["per_workload"] = cpu_oracle_configs()
 
     out = {
         "metric": METRIC,

@@ -128,3 +128,28 @@ def test_issue_counter_summary_from_synthetic_passes(tmp_path):
     # co-issue 800/3200, waits 300/1000 and 250/1000, active 450/1000, 4.6 / 2.3 / 1.5 per MFMA
     assert "| `attn_dkdv_pair_kernel<128>` | 1048576 | 25% | 30% | 25% | 45% | 4.60 | 2.30 | 1.50 | 0 |" in md
     assert "pass a\npass b" in md
+
+
+def test_suites_summary_from_a_bench_line(tmp_path):
+    """The --summarize-suites tables come from a bench JSON line alone (no GPU)."""
+    import json
+    import bench
+    line = {"value": 900.0, "steps": 20, "ms_per_step": 4.2, "per_kernel_ms": {"attn_fwd": 1.0},
+            "roofline": {"kernel": "attn_dkdv_pair_kernel", "achieved": 1200.0, "frac": 0.48, "peak": 2516.6},
+            "timing_spread": {"per_step_ms": {"median": 4.2, "q1": 4.1, "q3": 4.3}},
+            "decode_suite": {"rows": [{"B": 8, "keys": 65536, "Hkv": 8, "us_per_call": 300.0, "gbs": 6000.0,
+                                       "workspace_bytes": 2**21, "output_bytes": 65536 + 1024,
+                                       "device_peak_bytes": 3 * 2**20}]},
+            "memory": {"device_peak": {"rows": [{"T": 1024, "device_peak_mb": 3.0, "inputs_mb": 32.0}]},
+                       "residuals": {"rows": [{"T": 1024, "residual_mb": 2.06}]}},
+            "cpu_baseline": {"value": 0.12, "cores": 16, "sample": "s", "blas": "openblas",
+                             "per_workload": {"unit": "ms", "threads": 16, "rows": [
+                                 {"workload": "fp32_mha_T128_d64", "sample": "whole workload", "calls": 3,
+                                  "fwd_ms": 0.5, "fwd_bwd_ms": 2.0, "fwd_ms_1thread": 0.6,
+                                  "fwd_bwd_ms_1thread": 2.4}]}}}
+    log = tmp_path / "bench.log"
+    log.write_text("progress\n" + json.dumps(line) + "\n")
+    bench.summarize_suites(str(log), "python3 bench.py --suites", out_dir=str(tmp_path))
+    text = (tmp_path / "suites_and_legs.md").read_text()
+    assert "| 8 | 65536 | 8 | 300.0 | 6000.0 | 2.00 |" in text
+    assert "python3 bench.py --suites" in text and "openblas" in text and "| 1024 | 2.06 |" in text

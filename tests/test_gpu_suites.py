@@ -60,3 +60,34 @@ def test_gqa_suite_native_equals_repeated_kv():
 @pytest.mark.parametrize("key", [(8, 4096, 8), (8, 4096, 32), (1, 65536, 8)], ids=lambda k: f"B{k[0]}_kv{k[1]}_hkv{k[2]}")
 def test_decode_suite(key):
     check_decode(DECODE[key])
+
+
+@pytest.mark.parametrize("hkv", [8, 32])
+def test_decode_suite_peak_point_B8_64k_keys(hkv):
+    """The pages' decode peak point: batch 8, 64k keys, 32 query heads, one
+    query each, full caches ("Attention performance", section
+    "Grouped-query attention and decoding"; the pages ran it with 8 KV heads).
+    Two seeded batches are repeated along the batch axis on the device, so the
+    host holds the oracle's inputs for two batches only; those two are checked
+    against the oracle, and every batch must equal its source bit for bit
+    (equal lengths give every batch the same key ranges and merge order)."""
+    import torch
+    from forward_backward_amd import attn
+    from forward_backward_amd.inputs import Case
+    src = Case(f"dec_peak_src_hkv{hkv}", 2, 1, 65536, 32, hkv, 128, workload_id=610 + hkv, decode=True)
+    host, dev, f64 = device_inputs(src, with_do=False)
+    B = 8
+    print(f"[decode peak point] B{B} keys {src.Tkv} Hkv {hkv}", flush=True)
+    idx = torch.arange(B, device="cuda") % src.B
+    q, k, v = (torch.index_select(dev[n], 0, idx).contiguous() for n in ("q", "k", "v"))
+    o, lse = attn.decode(q, k, v, scale=src.scale)
+    torch.cuda.synchronize()
+    for name, bits in (("o", o.view(torch.int16)), ("lse", lse.view(torch.int32))):
+        assert torch.equal(bits, torch.index_select(bits[:src.B], 0, idx)), f"{name}: a batch differs from its source"
+    del k, v
+    from helpers import oracle_full
+    ref = oracle_full(src, f64, bwd=False)
+    err = rel_err(to_host64(o[:src.B]), ref["o"])
+    print(f"    o rel err {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    check_lse(to_host64(lse[:src.B]), ref["lse"])
