@@ -84,7 +84,7 @@ __device__ __forceinline__ float half_sum(float x) {
 // At D=256 a row spans two bank lines and the D=128 pattern applies to the
 // low four bits of the chunk index.
 template <int D>
-__device__ __forceinline__ int swz_f(int r) {
+__host__ __device__ __forceinline__ int swz_f(int r) {
   static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head_dim 32, 64, 128 or 256");
   if constexpr (D >= 128) {
     return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -97,7 +97,7 @@ __device__ __forceinline__ int swz_f(int r) {
 
 // Element offset of logical (row, col) in a swizzled tile; col % 4 == 0.
 template <int D>
-__device__ __forceinline__ int swz_off(int r, int col) {
+__host__ __device__ __forceinline__ int swz_off(int r, int col) {
   return r * D + ((((col >> 3) ^ swz_f<D>(r))) << 3) + (col & 7);
 }
 
@@ -144,6 +144,44 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
       : "memory");
 }
 
+// Geometry of the copy of a swizzled [ROWS, D] bf16 tile by THREADS threads:
+// each wave copies 1 KiB blocks, one 16-byte chunk per lane, lane i of a
+// block landing at LDS byte 16 i of it. Copy i of wave w fills block
+// i * WAVES + w; a lane fetches the logical chunk that the swizzle puts at its
+// physical place. Shared by the copy paths below and by a host-compiled
+// bounds model in the tests.
+template <int D, int ROWS, int THREADS>
+struct TileGeom {
+  static constexpr int RPW = 1024 / (2 * D);  // rows per block
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int WAVES = THREADS / 64;
+  static constexpr int ITERS = ROWS / (RPW * WAVES);
+  static_assert(ROWS % (RPW * WAVES) == 0, "tile rows must split evenly over the waves");
+  __host__ __device__ static int block(int i, int wave) { return i * WAVES + wave; }
+  __host__ __device__ static int row(int i, int wave, int lane) { return block(i, wave) * RPW + lane / CPR; }
+  __host__ __device__ static int chunk(int r, int lane) { return (lane % CPR) ^ swz_f<D>(r); }
+  // Element offset of the lane's chunk in row `gr` of a matrix with row stride rs.
+  __host__ __device__ static long elem(long gr, int r, int lane, long rs) { return gr * rs + chunk(r, lane) * 8; }
+  // Byte offset of the lane's chunk from the tile's first row (32 bits: the
+  // API bounds heads * head_dim, so (ROWS - 1) * rs * 2 + 2 * D < 2^32).
+  __host__ __device__ static uint32_t voff(int i, int wave, int lane, long rs) {
+    const int r = row(i, wave, lane);
+    return static_cast<uint32_t>(elem(r, r, lane, rs) * 2);
+  }
+  // Row a lane of a partial tile reads: rows at or past rlim (>= 1) re-read rlim - 1.
+  __host__ __device__ static int clamp_row(int r0, int r, int rlim) {
+    const int gr = r0 + r;
+    return gr < rlim ? gr : rlim - 1;
+  }
+};
+
+// A 64-bit address from its two 32-bit halves, each taken as unsigned (the
+// halves come back from readfirstlane as signed ints; a signed widening of the
+// low half would spread its bit 31 over the high half).
+__host__ __device__ __forceinline__ uint64_t join_halves(uint32_t lo, uint32_t hi) {
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Asynchronous global -> LDS copy of rows [r0, r0 + ROWS) of a bf16 matrix
 // with row stride `rs` elements into a swizzled [ROWS, D] LDS tile, by the
 // THREADS threads of the workgroup: each wave copies 1 KiB per instruction,
@@ -155,23 +193,17 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
 // one array apart and waits before transpose reads in particular).
 template <int D, int ROWS, int THREADS, bool VISIBLE = false>
 __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long rs, int r0, int rlim, int tid) {
-  constexpr int RPW = 1024 / (2 * D);  // rows per wave per instruction
-  constexpr int CPR = D / 8;
-  constexpr int WAVES = THREADS / 64;
-  constexpr int ITERS = ROWS / (RPW * WAVES);
-  static_assert(ROWS % (RPW * WAVES) == 0, "tile rows must split evenly over the waves");
+  using Gm = TileGeom<D, ROWS, THREADS>;
   const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int i = 0; i < ITERS; ++i) {
-    const int wi = i * WAVES + wave;
-    const int r = wi * RPW + lane / CPR;
-    const int c = (lane % CPR) ^ swz_f<D>(r);
-    int gr = r0 + r;
-    gr = gr < rlim ? gr : rlim - 1;
+  for (int i = 0; i < Gm::ITERS; ++i) {
+    const int r = Gm::row(i, wave, lane);
+    const uint16_t* src = g + Gm::elem(Gm::clamp_row(r0, r, rlim), r, lane, rs);
+    uint16_t* dst = tile + Gm::block(i, wave) * 512;
     if constexpr (VISIBLE)
-      __builtin_amdgcn_global_load_lds((const void*)(g + gr * rs + c * 8), (lds_void_t*)(tile + wi * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)dst, 16, 0, 0);
     else
-      dma16(g + gr * rs + c * 8, lds_addr(tile + wi * 512));
+      dma16(src, lds_addr(dst));
   }
 }
 
@@ -185,7 +217,7 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
-  const void* sbase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const void* sbase = reinterpret_cast<const void*>(join_halves(lo, hi));
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -222,7 +254,7 @@ __device__ __forceinline__ void dma16_batch(const void* base_a, const void* base
     const uint64_t u = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32)));
-    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return reinterpret_cast<const void*>(join_halves(lo, hi));
   };
   const void* sa = uniform(base_a);
   const uint32_t l0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
@@ -271,22 +303,18 @@ __device__ __forceinline__ void dma16_batch(const void* base_a, const void* base
 // one uniform base pointer. Needs (ROWS - 1) * rs * 2 + 2 * D < 2^32 bytes.
 template <int D, int ROWS, int THREADS>
 struct TileCopy {
-  static constexpr int RPW = 1024 / (2 * D);
-  static constexpr int CPR = D / 8;
-  static constexpr int WAVES = THREADS / 64;
-  static constexpr int ITERS = ROWS / (RPW * WAVES);
-  static_assert(ROWS % (RPW * WAVES) == 0, "tile rows must split evenly over the waves");
+  using Gm = TileGeom<D, ROWS, THREADS>;
+  static constexpr int RPW = Gm::RPW;
+  static constexpr int CPR = Gm::CPR;
+  static constexpr int WAVES = Gm::WAVES;
+  static constexpr int ITERS = Gm::ITERS;
   uint32_t voff[ITERS];  // byte offset of this lane's chunk from the tile's first row
   uint32_t lds_wave;     // byte offset of this wave's first 1 KiB block in the tile (uniform)
 
   __device__ __forceinline__ TileCopy(long rs, int tid) {
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int r = (i * WAVES + wave) * RPW + lane / CPR;
-      const int c = (lane % CPR) ^ swz_f<D>(r);
-      voff[i] = (uint32_t)((r * rs + c * 8) * 2);
-    }
+    for (int i = 0; i < ITERS; ++i) voff[i] = Gm::voff(i, wave, lane, rs);
     lds_wave = __builtin_amdgcn_readfirstlane(wave * 1024);
   }
 
@@ -390,7 +418,7 @@ __host__ __device__ __forceinline__ void tile_order(int bid, int ntiles, int nun
   }
 }
 
-__device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int tkv) {
+__host__ __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int tkv) {
   if (kv_lens == nullptr) return tkv;
   int n = kv_lens[b];
   return n < 0 ? 0 : (n > tkv ? tkv : n);
@@ -401,8 +429,8 @@ __device__ __forceinline__ int clamp_len(const int32_t* kv_lens, int b, int tkv)
 // (i - left <= j <= i + right; -1 = no bound on that side). Both bounds are
 // non-decreasing in i, so a tile of rows [r0, r1] touches keys
 // [key_lo(r0), key_hi(r1)] and every key of [key_lo(r1), key_hi(r0)].
-__device__ __forceinline__ int key_lo(int i, int left) { return left < 0 ? 0 : max(i - left, 0); }
-__device__ __forceinline__ int key_hi(int i, int kvlim, int causal, int right) {
+__host__ __device__ __forceinline__ int key_lo(int i, int left) { return left < 0 ? 0 : max(i - left, 0); }
+__host__ __device__ __forceinline__ int key_hi(int i, int kvlim, int causal, int right) {
   int hi = kvlim - 1;
   if (causal) hi = min(hi, i);
   if (right >= 0) hi = min(hi, i + right);
