@@ -128,13 +128,30 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
   const int ntiles = nh * nq;
 
   if (k0 < kvlim && ntiles > 0) {
-    // K (S wave) or V (dP wave) rows of this lane's key as B operands.
+    // K (S wave) or V (dP wave) rows of this lane's key as B operands. At
+    // head_dim 128 the workgroup's 128 K and V rows go through LDS (areas free
+    // until the first hand-over and the first in-loop copy) by the coalesced
+    // tile copy: loaded lane by lane, each instruction touched 32 rows and the
+    // tile copies queued behind them (about 2 us per workgroup).
     u32x4_t frag[C::KS];
     const bool key_ok = key < kvlim;
-    const uint16_t* src = role == 0 ? (const uint16_t*)a.k : (const uint16_t*)a.v;
+    uint16_t* const k_lds = (uint16_t*)(smem + X_OFF);          // 128 x D: the hand-over slots
+    uint16_t* const v_lds0 = q_st + (C::NST - 1) * C::TILE;     // keys 0..63: the last Q stage
+    uint16_t* const v_lds1 = g_st + (C::NST - 1) * C::TILE;     // keys 64..127: the last dO stage
+    if constexpr (TWO) {
+      static_assert(!TWO || (XN * XB == 2 * 64 * D * 2 && C::BM == 64 && C::BN == 128), "K/V staging areas");
+      const uint16_t* kg = (const uint16_t*)a.k + kvoff;
+      const uint16_t* vg = (const uint16_t*)a.v + kvoff;
+      dma_tile<D, 64, C::THREADS>(k_lds, kg, krs, k0, kvlim, tid);
+      dma_tile<D, 64, C::THREADS>(k_lds + 64 * D, kg, krs, k0 + 64, kvlim, tid);
+      dma_tile<D, 64, C::THREADS>(v_lds0, vg, krs, k0, kvlim, tid);
+      dma_tile<D, 64, C::THREADS>(v_lds1, vg, krs, k0 + 64, kvlim, tid);
+    } else {
+      const uint16_t* src = role == 0 ? (const uint16_t*)a.k : (const uint16_t*)a.v;
 #pragma unroll
-    for (int t = 0; t < C::KS; ++t)
-      frag[t] = key_ok ? gload16(src + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+      for (int t = 0; t < C::KS; ++t)
+        frag[t] = key_ok ? gload16(src + kvoff + key * krs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    }
     const float c = a.scale_log2;
     const int tr_row = 4 * hh + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -280,6 +297,16 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
     }
     wait_vmem();
     __syncthreads();
+    if constexpr (TWO) {
+      // Every wave takes its fragments before the hand-over slots and the last
+      // stages are written.
+      const int r = 32 * w4 + l32;  // row of the lane's key in the 128-key tile
+      const uint16_t* kv = role == 0 ? k_lds + (r >> 6) * 64 * D : (r < 64 ? v_lds0 : v_lds1);
+#pragma unroll
+      for (int t = 0; t < C::KS; ++t)
+        frag[t] = key_ok ? lds_read16(kv + swz_off<D>(r & 63, 16 * t + 8 * hh)) : u32x4_t{0, 0, 0, 0};
+      __syncthreads();
+    }
     const int nb = C::BPT * ntiles;  // 32-row blocks
     // Ring bookkeeping shared by both roles (same barriers in the same order).
     // Step i reads blocks i and i + 1, so tile u (blocks BPT u ..) is read in
