@@ -117,19 +117,32 @@ def _short_name(kernel_name):
     return re.sub(r"\(.*", "", k)
 
 
-def _read_counter_csv(directory, counter):
-    """Per-kernel list of per-dispatch values of `counter` from a rocprofv3 --pmc CSV."""
+def _read_counter_csv(directory, counter, first_leg=0):
+    """Per-kernel list of per-dispatch values of `counter` from a rocprofv3 --pmc CSV.
+
+    With first_leg > 0 only the first `first_leg` dispatches of each non-decode
+    kernel count (bench.py runs the headline leg first; the causal, window and
+    other legs launch the same kernels on other workloads). Decode kernels
+    only ever run the one decode workload, so all their dispatches count.
+    """
     import csv
     import glob
-    out = {}
+    per = {}
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
-        per = {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             key = (_short_name(r["Kernel_Name"]), int(r["Dispatch_Id"]), r["Grid_Size"])
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-        for (name, _, grid), v in per.items():
+    by_name = {}
+    for (name, did, grid), v in per.items():
+        by_name.setdefault(name, []).append((did, grid, v))
+    out = {}
+    for name, ds in by_name.items():
+        ds.sort()
+        if first_leg and not name.startswith("attn_decode") and "copyBuffer" not in name:
+            ds = ds[:first_leg]
+        for _, grid, v in ds:
             out.setdefault((name, grid), []).append(v)
     return out
 
@@ -183,8 +196,10 @@ def summarize(stats_dir, fetch_dir, write_dir, command, counter_command, out_dir
     with open(os.path.join(prof, "fwd_bwd_d128_T8192_kernel_stats.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    fetch = _read_counter_csv(fetch_dir, "FETCH_SIZE")
-    write = _read_counter_csv(write_dir, "WRITE_SIZE")
+    cw = int((_re.search(r"--warmup (\d+)", counter_command or "") or [None, 3])[1])
+    ck = int((_re.search(r"--steps (\d+)", counter_command or "") or [None, 20])[1])
+    fetch = _read_counter_csv(fetch_dir, "FETCH_SIZE", cw + ck)
+    write = _read_counter_csv(write_dir, "WRITE_SIZE", cw + ck)
     copy_f = [v for (n, g), vs in fetch.items() if "copyBuffer" in n for v in vs]
     copy_w = [v for (n, g), vs in write.items() if "copyBuffer" in n for v in vs]
     copy_kib = None
@@ -193,10 +208,12 @@ def summarize(stats_dir, fetch_dir, write_dir, command, counter_command, out_dir
         copy_kib = max(copy_w)
     f_factor = copy_kib / max(copy_f) if copy_f and copy_kib else None
     w_factor = 1.0 if copy_kib else None
-    lines = ["# HBM traffic per dispatch: attention fwd+bwd B4 H8 d128 T8192, non-causal", "",
+    lines = ["# HBM traffic per dispatch: attention fwd+bwd B4 H8 d128 T8192 non-causal, and GQA decode", "",
              "Two rocprofv3 counter passes of the command below, one with FETCH_SIZE, one with WRITE_SIZE (KiB "
              "per dispatch), each scaled by what the counter reads for a plain device copy of known size run in "
-             "the same process (`--copy-calibration 256`: 256 MiB read, 256 MiB written).", "",
+             "the same process (`--copy-calibration 256`: 256 MiB read, 256 MiB written). The fwd/bwd rows are "
+             "the headline leg's dispatches (the run's first leg); the decode rows are every dispatch of the "
+             "decode leg (batch 4, 16 query rows, 16384-key caches, 32 query heads over 8 KV heads).", "",
              "```", counter_command or "", "```", "",
              f"Copy calibration: WRITE_SIZE {copy_kib} KiB for 262144 KiB written (factor {w_factor}); "
              f"FETCH_SIZE {max(copy_f) if copy_f else None} KiB for 262144 KiB read (factor {f_factor}).", "",

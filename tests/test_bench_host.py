@@ -79,6 +79,31 @@ def test_summaries_from_synthetic_rocprof_output(tmp_path):
     assert "| 2000.0 | 2.10 | 50.0% |" in mfma_md
 
 
+def test_traffic_counts_the_headline_leg_and_every_decode_dispatch(tmp_path):
+    """Later legs launch the tile kernels on other workloads with the same grid; they must not be averaged in."""
+    stats, fetch, write, out = (str(tmp_path / n) for n in ("stats", "fetch", "write", "out"))
+    os.makedirs(out)
+    _write_csv(os.path.join(stats, "run_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"], [])
+    _write_csv(os.path.join(stats, "run_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], [])
+    split = "void attn::(anonymous namespace)::attn_decode_split_kernel<128>(attn::DecodeArgs)"
+    # --warmup 1 --steps 2: dispatches 2-4 are the headline leg (300000 KiB each), 5-7 the causal leg
+    # (same grid, 150000 KiB); the decode kernel runs twice later, 1000 and 3000 KiB.
+    f_rows = [(COPY, 1, 4096, "FETCH_SIZE", 131072.0)]
+    f_rows += [(DKDV, d, 524288, "FETCH_SIZE", 300000.0 if d < 5 else 150000.0) for d in range(2, 8)]
+    f_rows += [(split, 8, 1024, "FETCH_SIZE", 1000.0), (split, 9, 1024, "FETCH_SIZE", 3000.0)]
+    _counters(os.path.join(fetch, "run_counter_collection.csv"), f_rows)
+    w_rows = [(COPY, 1, 4096, "WRITE_SIZE", 262144.0)]
+    w_rows += [(DKDV, d, 524288, "WRITE_SIZE", 100000.0 if d < 5 else 10.0) for d in range(2, 8)]
+    w_rows += [(split, 8, 1024, "WRITE_SIZE", 10.0), (split, 9, 1024, "WRITE_SIZE", 30.0)]
+    _counters(os.path.join(write, "run_counter_collection.csv"), w_rows)
+    bench.summarize(stats, fetch, write, "python3 bench.py --warmup 1 --steps 2",
+                    "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --warmup 1 --steps 2", out_dir=out)
+    kern = json.load(open(os.path.join(out, "hbm_traffic.json")))["kernels"]
+    assert kern["attn_dkdv_pair_kernel"]["bytes_per_launch"] == (300000 * 2 + 100000) * 1024
+    assert kern["attn_decode_split_kernel"]["bytes_per_launch"] == (2000 * 2 + 20) * 1024
+
+
 def test_stored_traffic_needs_the_current_sources(tmp_path):
     path = str(tmp_path / "hbm_traffic.json")
     rec = {"source_digest": bench.source_digest(), "kernels": {"attn_dkdv_pair_kernel": {"bytes_per_launch": 7}}}
