@@ -40,8 +40,15 @@ COMMON = [
 # v_accvgpr_read per step for the softmax): 13% faster at 32 and 9% at 64, same
 # occupancy. On the head_dim 256 kernels the same option measured 18% slower.
 # The decode kernels too: the split kernel at C5 45.3 -> 44.8 us per call.
+# The persistent head_dim 128 dK/dV kernel is scheduled with the iterative
+# max-occupancy strategy: under the default and max-ILP strategies its step
+# loops waited for each LDS read before the product that uses it (18 and 15
+# full LDS drains per S-wave step against 11), and the kernel ran 3-5% slower
+# than with one workgroup per item; with it, 0.9% faster than that at B4 H8
+# d128 T8192, 2% causal, 7.5% with a 1024-key window, 15% with KV lengths.
 PER_FILE = {
     "attn_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_dkdv_queue.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-maxocc"],
     "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "attn_dkdv_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -128,9 +128,12 @@ static size_t bwd_part_bytes(const attn_params_t* p) {
   return round_up(2 * (size_t)s * p->B * p->Tkv * p->Hkv * p->D * sizeof(float), 256);
 }
 
+// Work counters of the dK/dV pass, after the row statistics and partials.
+static constexpr size_t kQueueBytes = attn::kBwdQueueWords * sizeof(unsigned);
+
 size_t attn_bwd_workspace_size(const attn_params_t* p) {
   if (p == nullptr) return 0;
-  return 6 * bwd_stat_bytes(p) + bwd_part_bytes(p);
+  return 6 * bwd_stat_bytes(p) + bwd_part_bytes(p) + kQueueBytes;
 }
 
 attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -178,6 +181,8 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
   a.dkv_part = a.kv_split > 1
                    ? reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ws)) + 6 * bwd_stat_bytes(p))
                    : nullptr;
+  a.queue = reinterpret_cast<unsigned*>(static_cast<char*>(const_cast<void*>(ws)) + 6 * bwd_stat_bytes(p) +
+                                        bwd_part_bytes(p));
   a.kv_lens = p->kv_lens;
   a.B = p->B; a.Tq = p->Tq; a.Tkv = p->Tkv; a.Hq = p->Hq; a.Hkv = p->Hkv;
   a.scale = p->scale; a.scale_log2 = p->scale * kLog2e; a.causal = p->causal;
@@ -211,7 +216,7 @@ attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const f
 }
 
 attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
-                            const void* dout, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                            const void* dout, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                             void* stream) {
   attn::BwdArgs a;
   attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);

@@ -26,40 +26,34 @@ namespace attn {
 void launch_delta_any(const BwdArgs& a, int D, bool bf16, hipStream_t s);
 void launch_dq_bf16(const BwdArgs& a, int D, hipStream_t s);  // attn_dq.hip
 void launch_dkdv_bf16_small(const BwdArgs& a, int D, hipStream_t s);  // head_dim 32 and 64, attn_dkdv_small.hip
+void launch_dkdv_queue(const BwdArgs& a, hipStream_t s);  // head_dim 128, attn_dkdv_queue.hip
 
 namespace {
 
-// dK/dV at head_dim 128 and 256 with the work of each 32-key block split over
-// a pair of waves, so that every wave holds half the state (K or V rows, dV or
-// dK): at head_dim 128 two waves share each SIMD (the single-role kernel holds
-// both and runs one wave per SIMD; at head_dim 64 and 32 it stays the faster
-// one); at head_dim 256 one wave per SIMD holds all 256 columns of its dV or
-// dK, so S and dP are formed once per block:
+// dK/dV at head_dim 256 with the work of each 32-key block split over a pair
+// of waves, so that every wave holds half the state (K or V rows, dV or dK):
+// one wave per SIMD holds all 256 columns of its dV or dK, so S and dP are
+// formed once per block:
 //   S wave:  K rows (B operand) and dV^T; per 32-row block S = Q K^T,
 //            P = exp2(c S'), P (bf16) to LDS for its partner,
 //            dV^T += dO^T P
 //   dP wave: V rows and dK^T; dP = dO V^T, P from LDS,
 //            dS = P dP', dK^T += Q^T dS
-// At head_dim 256 (32-row tiles) both roles run the same products: in step i
-// the row product (S or dP) of block i + 1 beside the transposed product (dV
-// or dK) of block i, whose B operand (P or dS) came from the previous step; one
-// workgroup barrier per step hands P over (double-buffered). At head_dim 128
-// (64-row tiles of two blocks) a step covers a tile, with one barrier: the S
-// wave runs, block by block, the row product of tile j + 1 beside the
-// transposed product of tile j; the dP wave forms dP' and dS of tile j's blocks
-// in the step (P from the previous step, four hand-over slots). The Q/dO/
-// row-term ring is that of the single-role kernel (three stages; the copy of a
-// tile starts two tiles ahead and has landed by the end of the next step).
+// Both roles run the same products: in step i the row product (S or dP) of
+// block i + 1 beside the transposed product (dV or dK) of block i, whose B
+// operand (P or dS) came from the previous step; one workgroup barrier per
+// step hands P over (double-buffered). Head_dim 128 runs the same split of
+// work in the persistent kernel of attn_dkdv_queue.hip.
 template <int D>
 struct DkvPairCfg {
-  // head_dim 128: 4 pairs (two waves per SIMD), 64-row tiles, 3 stages.
-  // head_dim 256: 2 pairs (one wave per SIMD: a wave holds 64 registers of K
-  // or V and 128 of dV or dK), 32-row tiles, 4 stages.
-  static constexpr int NP = D > 128 ? 2 : 4;        // wave pairs, 32 keys each
+  // 2 pairs (one wave per SIMD: a wave holds 64 registers of K or V and 128
+  // of dV or dK), 32-row tiles, 4 stages.
+  static_assert(D == 256, "the wave-pair kernel runs head_dim 256");
+  static constexpr int NP = 2;                      // wave pairs, 32 keys each
   static constexpr int BN = 32 * NP;                // keys per workgroup
-  static constexpr int BM = D > 128 ? 32 : 64;      // query rows per LDS tile
+  static constexpr int BM = 32;                     // query rows per LDS tile
   static constexpr int BPT = BM / 32;               // 32-row blocks per tile
-  static constexpr int NST = D > 128 ? 4 : 3;       // LDS stages
+  static constexpr int NST = 4;                     // LDS stages
   static constexpr int THREADS = 128 * NP;          // NP S waves, then NP dP waves
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -76,10 +70,7 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
   constexpr int R_OFF = 0;                        // row terms: 16 bytes per query row
   constexpr int Q_OFF = C::NST * C::BM * 16;      // Q stages
   constexpr int G_OFF = Q_OFF + C::NST * TB;      // dO stages
-  // With two 32-row blocks per tile (head_dim 128) a step covers a whole tile:
-  // both blocks between two barriers, their P in slots blk % 4.
-  constexpr bool TWO = C::BPT == 2;
-  constexpr int XN = TWO ? 4 : 2;                 // hand-over slots
+  constexpr int XN = 2;                           // hand-over slots
   constexpr int X_OFF = G_OFF + C::NST * TB;      // P hand-over: [XN][NP waves][2 halves][64 lanes] x 16 B
   constexpr int XB = C::NP * 2 * 1024;            // bytes of one hand-over slot
   __shared__ __attribute__((aligned(16))) char smem[X_OFF + XN * XB];
@@ -128,25 +119,10 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
   const int ntiles = nh * nq;
 
   if (k0 < kvlim && ntiles > 0) {
-    // K (S wave) or V (dP wave) rows of this lane's key as B operands. At
-    // head_dim 128 the workgroup's 128 K and V rows go through LDS (areas free
-    // until the first hand-over and the first in-loop copy) by the coalesced
-    // tile copy: loaded lane by lane, each instruction touched 32 rows and the
-    // tile copies queued behind them (about 2 us per workgroup).
+    // K (S wave) or V (dP wave) rows of this lane's key as B operands.
     u32x4_t frag[C::KS];
     const bool key_ok = key < kvlim;
-    uint16_t* const k_lds = (uint16_t*)(smem + X_OFF);          // 128 x D: the hand-over slots
-    uint16_t* const v_lds0 = q_st + (C::NST - 1) * C::TILE;     // keys 0..63: the last Q stage
-    uint16_t* const v_lds1 = g_st + (C::NST - 1) * C::TILE;     // keys 64..127: the last dO stage
-    if constexpr (TWO) {
-      static_assert(!TWO || (XN * XB == 2 * 64 * D * 2 && C::BM == 64 && C::BN == 128), "K/V staging areas");
-      const uint16_t* kg = (const uint16_t*)a.k + kvoff;
-      const uint16_t* vg = (const uint16_t*)a.v + kvoff;
-      dma_tile<D, 64, C::THREADS>(k_lds, kg, krs, k0, kvlim, tid);
-      dma_tile<D, 64, C::THREADS>(k_lds + 64 * D, kg, krs, k0 + 64, kvlim, tid);
-      dma_tile<D, 64, C::THREADS>(v_lds0, vg, krs, k0, kvlim, tid);
-      dma_tile<D, 64, C::THREADS>(v_lds1, vg, krs, k0 + 64, kvlim, tid);
-    } else {
+    {
       const uint16_t* src = role == 0 ? (const uint16_t*)a.k : (const uint16_t*)a.v;
 #pragma unroll
       for (int t = 0; t < C::KS; ++t)
@@ -194,40 +170,6 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
         i = i < a.Tq ? i : a.Tq - 1;
         dma16(a.rowstat + (((long)b * a.Hq + h) * a.Tq + i) * 8, lds_addr(r_st + st * C::BM * 8));
       }
-    };
-    // In-order issue of the tiles (TWO path): tile t is query tile
-    // qt_begin + t % nq of head h_lo + t / nq, and the copies go out for
-    // t = 0, 1, ... in turn, so the tile, head and stage counters advance by
-    // one per call instead of being divided out of t.
-    int iss_q = 0, iss_st = 0;
-    const long hbase = (long)b * a.Tq * a.Hq + kh * G + h_lo;
-    const uint16_t* iss_qh = (const uint16_t*)a.q + hbase * D;
-    const uint16_t* iss_gh = (const uint16_t*)a.dout + hbase * D;
-    const uint16_t* iss_rh = a.rowstat + (((long)b * a.Hq + kh * G + h_lo) * a.Tq) * 8;
-    auto issue_next = [&]() {
-      const int q0 = (qt_begin + iss_q) * C::BM;
-      uint16_t* qs = q_st + iss_st * C::TILE;
-      if (q0 + C::BM <= a.Tq) {
-        qcopy.template copy2<G_OFF - Q_OFF>(qs, iss_qh, iss_gh, qrs, q0);
-      } else {
-        dma_tile<D, C::BM, C::THREADS>(qs, iss_qh, qrs, q0, a.Tq, tid);
-        dma_tile<D, C::BM, C::THREADS>(g_st + iss_st * C::TILE, iss_gh, qrs, q0, a.Tq, tid);
-      }
-      if (wave == 0 && lane < C::BM) {
-        const int i = min(q0 + lane, a.Tq - 1);
-        dma16(iss_rh + (long)i * 8, lds_addr(r_st + iss_st * C::BM * 8));
-      }
-      iss_st = iss_st + 1 == C::NST ? 0 : iss_st + 1;
-      if (++iss_q == nq) {
-        iss_q = 0;
-        iss_qh += D;
-        iss_gh += D;
-        iss_rh += (long)a.Tq * 8;
-      }
-    };
-    auto mask_q0 = [&](int q0) {
-      return (wave_min_key < key_lo(q0 + C::BM - 1, a.win_left)) ||
-             (wave_max_key > key_hi(q0, kvlim, a.causal, a.win_right)) || (q0 + C::BM > a.Tq);
     };
     auto mask_tile = [&](int t) {
       if (t >= ntiles) return false;
@@ -289,49 +231,29 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
       return u32x4_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
     };
 
-    for (int t = 0; t < C::NST - 1 && t < ntiles; ++t) {
-      if constexpr (TWO)
-        issue_next();
-      else
-        issue(t);
-    }
+    for (int t = 0; t < C::NST - 1 && t < ntiles; ++t) issue(t);
     wait_vmem();
     __syncthreads();
-    if constexpr (TWO) {
-      // Every wave takes its fragments before the hand-over slots and the last
-      // stages are written.
-      const int r = 32 * w4 + l32;  // row of the lane's key in the 128-key tile
-      const uint16_t* kv = role == 0 ? k_lds + (r >> 6) * 64 * D : (r < 64 ? v_lds0 : v_lds1);
-#pragma unroll
-      for (int t = 0; t < C::KS; ++t)
-        frag[t] = key_ok ? lds_read16(kv + swz_off<D>(r & 63, 16 * t + 8 * hh)) : u32x4_t{0, 0, 0, 0};
-      __syncthreads();
-    }
     const int nb = C::BPT * ntiles;  // 32-row blocks
     // Ring bookkeeping shared by both roles (same barriers in the same order).
-    // Step i reads blocks i and i + 1, so tile u (blocks BPT u ..) is read in
-    // steps BPT u - 1 .. BPT u + BPT - 1. At the first step of tile t, tile
-    // t - 1 has been read for the last time and tile t - 1 + NST takes its
-    // stage: three steps (BPT 2, NST 3) or two (BPT 1, NST 4) before its
-    // first use, and the waits below make it land in time.
+    // Step i reads blocks (tiles) i and i + 1. At the first step of tile t,
+    // tile t - 1 has been read for the last time and tile t - 1 + NST takes
+    // its stage, two steps before its first use; the waits below make it land
+    // in time.
     auto step_begin = [&](int i) {
-      if (i % C::BPT == 0 && i / C::BPT - 1 + C::NST < ntiles) issue(i / C::BPT - 1 + C::NST);
+      if (i - 1 + C::NST < ntiles) issue(i - 1 + C::NST);
     };
     auto step_end = [&](int i) {
-      if constexpr (C::BPT == 2) {
-        if (i & 1) wait_vmem();  // the tile issued at step i - 1 has landed
+      // Tile i + 2 (issued at step i - 1) must land; the copies of tile i + 3
+      // issued at this step may stay in flight.
+      constexpr int CP = 2 * TileCopy<D, C::BM, C::THREADS>::ITERS;  // copy instructions per wave and tile
+      if (i + 3 < ntiles) {
+        if (wave == 0)
+          wait_vmcnt<CP + 1>();
+        else
+          wait_vmcnt<CP>();
       } else {
-        // Tile i + 2 (issued at step i - 1) must land; the copies of tile i + 3
-        // issued at this step may stay in flight.
-        constexpr int CP = 2 * TileCopy<D, C::BM, C::THREADS>::ITERS;  // copy instructions per wave and tile
-        if (i + 3 < ntiles) {
-          if (wave == 0)
-            wait_vmcnt<CP + 1>();
-          else
-            wait_vmcnt<CP>();
-        } else {
-          wait_vmem();
-        }
+        wait_vmem();
       }
       __syncthreads();
     };
@@ -364,97 +286,14 @@ __global__ __launch_bounds__(DkvPairCfg<D>::THREADS) void attn_dkdv_pair_kernel(
         const int t = blk / C::BPT;
         softmax_at(blk, s, mask_tile(t), t < ntiles ? tile_q0(t) : 0);
       };
-      if constexpr (TWO) {
-        // Step j: the transposed products of tile j's blocks 2j and 2j + 1
-        // (their P from the previous step) and the row products and softmax of
-        // tile j + 1's blocks, one block after the other, then one barrier.
-        u32x4_t pa[2], pb[2];
-        // Softmax walk: query tile of the tile whose P is formed next.
-        int sm_q = 0;
-        bool msk = mask_q0(qt_begin * C::BM);
-        int sq0 = qt_begin * C::BM;
-        auto sm_advance = [&](int t_next) {
-          if (++sm_q == nq) sm_q = 0;
-          sq0 = (qt_begin + sm_q) * C::BM;
-          msk = t_next < ntiles && mask_q0(sq0);
-        };
-        softmax_at(0, row_product_at(0, 0), msk, sq0);
-        pa[0] = pk[0];
-        pa[1] = pk[1];
-        softmax_at(1, row_product_at(0, 1), msk, sq0);
-        pb[0] = pk[0];
-        pb[1] = pk[1];
-        sm_advance(1);
-        __syncthreads();
-        int st_j = 0, st_n = 1 % C::NST;  // stages of tiles j and j + 1
-        for (int j = 0; j < ntiles; ++j) {
-          if (j + 2 < ntiles) issue_next();
-          // The S wave issues its row product at raised priority: its
-          // softmax, and through P the partner's next step, wait on it.
-          __builtin_amdgcn_s_setprio(1);
-          f32x16_t s = row_product_at(st_n, 0);
-          __builtin_amdgcn_s_setprio(0);
-          tr_product_at(st_j, 0, pa);
-          softmax_at(2 * j + 2, s, msk, sq0);
-          pa[0] = pk[0];
-          pa[1] = pk[1];
-          __builtin_amdgcn_sched_barrier(0);  // one block's state live at a time
-          s = row_product_at(st_n, 1);
-          tr_product_at(st_j, 1, pb);
-          softmax_at(2 * j + 3, s, msk, sq0);
-          pb[0] = pk[0];
-          pb[1] = pk[1];
-          sm_advance(j + 2);
-          st_j = st_n;
-          st_n = st_n + 1 == C::NST ? 0 : st_n + 1;
-          wait_vmem();  // tile j + 2 (issued above) is read from the next step on
-          __syncthreads();
-        }
-      } else {
-        softmax(0, row_product(0));
-        __syncthreads();
-        for (int i = 0; i < nb; ++i) {
-          step_begin(i);
-          const f32x16_t s = row_product(i + 1);
-          tr_product(i, pk);
-          softmax(i + 1, s);
-          step_end(i);
-        }
-      }
-    } else if constexpr (TWO) {
-      auto ds_of = [&](int blk, const f32x16_t& dp, u32x4_t (&pk)[2]) {
-        const uint32_t xo = x_off + (blk % XN) * XB;
-        const u32x4_t p0 = lds_read16((const uint16_t*)(smem + xo));
-        const u32x4_t p1 = lds_read16((const uint16_t*)(smem + xo + 1024));
-        float dsv[16];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          dsv[2 * w] = bf16_lo(p0[w]) * dp[2 * w];
-          dsv[2 * w + 1] = bf16_hi(p0[w]) * dp[2 * w + 1];
-          dsv[8 + 2 * w] = bf16_lo(p1[w]) * dp[8 + 2 * w];
-          dsv[8 + 2 * w + 1] = bf16_hi(p1[w]) * dp[8 + 2 * w + 1];
-        }
-        pk[0] = pack8(dsv);
-        pk[1] = pack8(dsv + 8);
-      };
-      // Step j: tile j's blocks one after the other, dP' and dS formed in the
-      // step (P from the previous step): no dP' is carried over a barrier (two
-      // carried blocks spilled), and the partner's vector work fills the wait
-      // on each block's row product.
+      softmax(0, row_product(0));
       __syncthreads();
-      int st_j = 0;  // stage of tile j
-      for (int j = 0; j < ntiles; ++j) {
-        if (j + 2 < ntiles) issue_next();
-        u32x4_t pk[2];
-        const f32x16_t dp0 = row_product_at(st_j, 0);
-        const f32x16_t dp1 = row_product_at(st_j, 1);
-        ds_of(2 * j, dp0, pk);
-        tr_product_at(st_j, 0, pk);
-        ds_of(2 * j + 1, dp1, pk);
-        tr_product_at(st_j, 1, pk);
-        st_j = st_j + 1 == C::NST ? 0 : st_j + 1;
-        wait_vmem();  // tile j + 2 (issued above) is read from the next step on
-        __syncthreads();
+      for (int i = 0; i < nb; ++i) {
+        step_begin(i);
+        const f32x16_t s = row_product(i + 1);
+        tr_product(i, pk);
+        softmax(i + 1, s);
+        step_end(i);
       }
     } else {
       f32x16_t dp = row_product(0);
@@ -551,11 +390,14 @@ void launch_pass(const BwdArgs& a, int pass, hipStream_t s) {
   } else if (pass == kBwdDkdv) {
     const long kblocks = (long)a.kv_split * a.num_ktiles * a.Hkv * a.B;
     if (kblocks > 0) {
-      if constexpr (D == 128 || D == 256)
+      if constexpr (D == 128) {
+        launch_dkdv_queue(a, s);
+      } else if constexpr (D == 256) {
         hipLaunchKernelGGL(attn_dkdv_pair_kernel<D>, dim3((unsigned)(kblocks * (kBwdBlockN / DkvPairCfg<D>::BN))),
                            dim3(DkvPairCfg<D>::THREADS), 0, s, a);
-      else
+      } else {
         launch_dkdv_bf16_small(a, D, s);
+      }
       if (a.kv_split > 1) {
         const long n8 = (long)a.B * a.Tkv * a.Hkv * D / 8;
         hipLaunchKernelGGL(attn_dkdv_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a, n8);

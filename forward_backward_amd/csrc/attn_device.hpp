@@ -371,6 +371,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Workgroups are dispatched round-robin over the 8 XCDs of the chip; map the
 // hardware id to a logical id so that each XCD gets a contiguous range of
 // logical ids (neighbouring tiles of one head then share that XCD's L2).
+// Index of the XCD (accelerator complex die) the calling wave runs on.
+__device__ __forceinline__ unsigned xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v;
+}
+
 __host__ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   constexpr int kXcds = 8;
   const int q = n / kXcds, r = n % kXcds;

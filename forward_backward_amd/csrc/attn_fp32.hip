@@ -908,6 +908,8 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(256) void attn_delta_kernel(BwdArgs a, long rows) {
   constexpr int TPR = D / 8;  // threads per row
   const long gt = (long)blockIdx.x * 256 + threadIdx.x;
+  // The work counters of the dK/dV pass start at zero.
+  if (blockIdx.x == 0 && threadIdx.x < kBwdQueueWords && a.queue != nullptr) a.queue[threadIdx.x] = 0u;
   const long row = gt / TPR;   // row index in [B, Tq, Hq] order
   const int part = (int)(gt % TPR);
   float acc = 0.f;
@@ -948,7 +950,7 @@ template <int D>
 void launch_delta(const BwdArgs& a, bool bf16, hipStream_t s) {
   const long rows = (long)a.B * a.Tq * a.Hq;
   const long threads = rows * (D / 8);
-  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  const unsigned blocks = threads > 0 ? (unsigned)((threads + 255) / 256) : 1u;  // one block zeroes the counters
   if (bf16)
     hipLaunchKernelGGL((attn_delta_kernel<D, true>), dim3(blocks), dim3(256), 0, s, a, rows);
   else
@@ -958,7 +960,7 @@ void launch_delta(const BwdArgs& a, bool bf16, hipStream_t s) {
 }  // namespace
 
 void launch_delta_any(const BwdArgs& a, int D, bool bf16, hipStream_t s) {
-  if ((long)a.B * a.Tq * a.Hq == 0) return;
+  if ((long)a.B * a.Tq * a.Hq == 0 && a.queue == nullptr) return;
   if (D == 128)
     launch_delta<128>(a, bf16, s);
   else if (D == 256)

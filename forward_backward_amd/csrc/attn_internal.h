@@ -48,6 +48,7 @@ struct BwdArgs {
   int kv_split;            // dK/dV workgroups per KV tile, each over heads_per_split query heads of the group
   int heads_per_split;
   float* dkv_part;         // workspace when kv_split > 1: fp32 partial dK then dV, [kv_split][B, Tkv, Hkv, D] each
+  unsigned* queue;         // workspace: kBwdQueueWords work counters, zero between passes
 };
 
 // Arguments of the split-KV decode kernels.
@@ -85,6 +86,7 @@ hipError_t decode_scratch(void** ptr);
 constexpr int kFwdBlockM = 128;   // query rows per forward workgroup
 constexpr int kBwdBlockM = 128;   // query rows per dQ workgroup
 constexpr int kBwdBlockN = 128;   // keys per dK/dV workgroup
+constexpr int kBwdQueueWords = 64;   // counters of the persistent dK/dV kernel (256 bytes of workspace)
 constexpr int kBwdFillTarget = 256;  // dK/dV workgroups below which a group's query heads are split (one per CU)
 constexpr int kDecodeTileN = 64;  // keys per decode iteration
 constexpr int kDecodeRows = 64;   // packed query rows per decode workgroup

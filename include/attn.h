@@ -106,7 +106,9 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
  * that reaches 256, at most Hq / Hkv) and the workspace adds two fp32
  * [S, B, Tkv, Hkv, D] arrays of partial dK and dV, summed in split order by
  * a reduction pass; S depends only on the shape, so results stay bitwise
- * reproducible. */
+ * reproducible. The last 256 bytes hold the work counters of the head_dim 128
+ * dK/dV pass (persistent workgroups taking 128-key tiles from a queue): the
+ * preprocess pass sets them to zero and the dK/dV pass leaves them at zero. */
 size_t attn_bwd_workspace_size(const attn_params_t* p);
 
 /* Backward: the gradients of a scalar loss with respect to Q, K and V given
@@ -130,13 +132,17 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
 /* The three passes of attn_bwd as separate calls, in the order attn_bwd
  * runs them (the split backward of "Attention performance", section "When
  * to use which"). attn_bwd_preprocess writes D = rowsum(dO * O) and LSE * log2(e)
- * into the workspace; attn_bwd_dkdv and attn_bwd_dq read them and are
- * independent of each other, so a caller may run them on two streams once
- * the preprocess has completed. Arguments mean what they mean for attn_bwd. */
+ * into the workspace (and zeroes its work counters); attn_bwd_dkdv and
+ * attn_bwd_dq read them and are independent of each other, so a caller may
+ * run them on two streams once the preprocess has completed. attn_bwd_dkdv
+ * also counts its work in the workspace's counters and returns them to zero,
+ * so the same workspace serves the next pass or a replay of a captured graph;
+ * two attn_bwd_dkdv calls must not run at the same time on one workspace.
+ * Arguments mean what they mean for attn_bwd. */
 attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const float* lse, const void* dout,
                                   void* workspace, size_t workspace_bytes, void* stream);
 attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
-                            const void* dout, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                            const void* dout, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                             void* stream);
 attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
                           const void* dout, void* dq, const void* workspace, size_t workspace_bytes, void* stream);

@@ -112,3 +112,49 @@ def test_dkdv_and_dq_on_two_streams_match_the_sequential_call(case):
 ], ids=lambda c: c.name)
 def test_bwd_wide_groups_and_many_short_sequences(case):
     check_bwd(case)
+
+
+@pytest.mark.parametrize("case", [
+    # Some KV tiles past the lengths (a batch of length 0): items without query
+    # rows are taken from the queue and stored as zeros.
+    Case("queue_d128_gqa_causal_kvlen", 3, 700, 700, 8, 2, 128, causal=True, kv_lens=(700, 0, 333), workload_id=127),
+    Case("queue_d128_T2048_window", 2, 2048, 2048, 4, 4, 128, causal=True, window=(300, 0), workload_id=128),
+], ids=lambda c: c.name)
+def test_dkdv_pass_repeats_and_graph_replays(case):
+    """The head_dim-128 dK/dV pass hands out its work through counters in the
+    workspace that the pre-pass zeroes and the pass leaves at zero: the pass
+    repeated without the pre-pass, and a captured backward replayed with
+    other work in between, give the eager call's gradients bit for bit."""
+    import torch
+    from forward_backward_amd import attn
+    host, dev, _ = device_inputs(case)
+    print(f"[dkdv repeats] {case.name}", flush=True)
+    kw = dict(scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"], window=case.window)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = attn.fwd(q, k, v, **kw)
+    dq_ref, dk_ref, dv_ref = attn.bwd(q, k, v, o, lse, do, **kw)
+    ws = attn.bwd_workspace(q, k, causal=case.causal, kv_lens=dev["kv_lens"], window=case.window)
+    attn.bwd_preprocess(o, lse, do, ws, q, k, **kw)
+    for _ in range(3):
+        dk, dv = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+        attn.bwd_dkdv(q, k, v, lse, do, ws, dk, dv, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(dk.view(torch.int16), dk_ref.view(torch.int16))
+        assert torch.equal(dv.view(torch.int16), dv_ref.view(torch.int16))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            out = attn.bwd(q, k, v, o, lse, do, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for t in out:
+            t.fill_(float("nan"))
+        attn.bwd(q, k, v, o, lse, do, **kw)  # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(out, (dq_ref, dk_ref, dv_ref)):
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
