@@ -137,11 +137,21 @@ def _read_counter_csv(directory, counter, first_leg=0):
     by_name = {}
     for (name, did, grid), v in per.items():
         by_name.setdefault(name, []).append((did, grid, v))
+    for ds in by_name.values():
+        ds.sort()
+    # The headline leg ends where the first attention kernel of the run (the
+    # forward) is dispatched for the first_leg + 1-th time.
+    bound = None
+    if first_leg:
+        attn = [(ds[0][0], name) for name, ds in by_name.items()
+                if name.startswith("attn") and not name.startswith("attn_decode")]
+        if attn:
+            lead = by_name[min(attn)[1]]
+            bound = lead[first_leg][0] if len(lead) > first_leg else None
     out = {}
     for name, ds in by_name.items():
-        ds.sort()
-        if first_leg and not name.startswith("attn_decode") and "copyBuffer" not in name:
-            ds = ds[:first_leg]
+        if bound is not None and not name.startswith("attn_decode") and "copyBuffer" not in name:
+            ds = [d for d in ds if d[0] < bound]
         for _, grid, v in ds:
             out.setdefault((name, grid), []).append(v)
     return out
@@ -184,9 +194,14 @@ def summarize(stats_dir, fetch_dir, write_dir, command, counter_command, out_dir
               f"{w} warmup + {k} timed steps; then the causal leg):", "",
               "| kernel | headline leg: dispatches | headline leg: average us (timed steps) | causal leg: average us |",
               "|---|---|---|---|"]
-    for name, ds in sorted(per_kernel.items()):
+    for ds in per_kernel.values():
         ds.sort()
-        if name.startswith("attn_decode"):
+    # Kernels first launched after the headline leg (short-sequence legs and
+    # the like) belong to other workloads.
+    lead = min((ds[0][0], name) for name, ds in per_kernel.items()) if per_kernel else None
+    leg_end = per_kernel[lead[1]][w + k][0] if lead and len(per_kernel[lead[1]]) > w + k else None
+    for name, ds in sorted(per_kernel.items()):
+        if name.startswith("attn_decode") or (leg_end is not None and ds[0][0] >= leg_end):
             continue
         head = [d for _, d in ds[:w + k]]
         timed = head[w:] if len(head) > w else head

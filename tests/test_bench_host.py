@@ -92,6 +92,9 @@ def test_traffic_counts_the_headline_leg_and_every_decode_dispatch(tmp_path):
     f_rows = [(COPY, 1, 4096, "FETCH_SIZE", 131072.0)]
     f_rows += [(DKDV, d, 524288, "FETCH_SIZE", 300000.0 if d < 5 else 150000.0) for d in range(2, 8)]
     f_rows += [(split, 8, 1024, "FETCH_SIZE", 1000.0), (split, 9, 1024, "FETCH_SIZE", 3000.0)]
+    # A kernel that only a later leg launches (another head_dim) is not part of the headline leg.
+    short = "void attn::(anonymous namespace)::attn_fwd_bf16_kernel<64>(attn::FwdArgs)"
+    f_rows += [(short, 10, 32768, "FETCH_SIZE", 5.0e6)]
     _counters(os.path.join(fetch, "run_counter_collection.csv"), f_rows)
     w_rows = [(COPY, 1, 4096, "WRITE_SIZE", 262144.0)]
     w_rows += [(DKDV, d, 524288, "WRITE_SIZE", 100000.0 if d < 5 else 10.0) for d in range(2, 8)]
@@ -100,6 +103,7 @@ def test_traffic_counts_the_headline_leg_and_every_decode_dispatch(tmp_path):
     bench.summarize(stats, fetch, write, "python3 bench.py --warmup 1 --steps 2",
                     "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --warmup 1 --steps 2", out_dir=out)
     kern = json.load(open(os.path.join(out, "hbm_traffic.json")))["kernels"]
+    assert "attn_fwd_bf16_kernel" not in kern
     assert kern["attn_dkdv_pair_kernel"]["bytes_per_launch"] == (300000 * 2 + 100000) * 1024
     assert kern["attn_decode_split_kernel"]["bytes_per_launch"] == (2000 * 2 + 20) * 1024
 
