@@ -43,7 +43,7 @@ def log(*a):
 
 
 KERNEL_SYMBOLS = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_preprocess": "attn_delta_kernel",
-                  "bwd_dkdv": "attn_dkdv_pair_kernel", "bwd_dq": "attn_dq_pair_kernel",
+                  "bwd_dkdv": "attn_dkdv_queue_kernel", "bwd_dq": "attn_dq_pair_kernel",
                   "decode_split": "attn_decode_split_kernel", "decode_combine": "attn_decode_combine_kernel"}
 
 
