@@ -305,6 +305,25 @@ __global__ __launch_bounds__(QTHREADS) void attn_dkdv_queue_kernel(BwdArgs a, in
     };
     bool nxt_ready = false;  // the item after `cur` is taken (and published in LDS)
     auto resolve = [&]() { nxt_ready = next_item(cs ^ 1); };
+    // The taker publishes the next item itself, before the barrier of a step
+    // (every wave reads it after that barrier); take_begin went out two steps
+    // earlier. An item without tiles still goes the way of next_item.
+    auto publish = [&]() {
+      const int id = take_end();
+      Item it;
+      it.nq = -1;
+      if (id >= 0) make_item(id, it);
+      items_s[cs ^ 1] = it;
+    };
+    auto collect = [&]() {
+      const int nq = __builtin_amdgcn_readfirstlane(items_s[cs ^ 1].nq);
+      if (nq == 0) {
+        store(read_item(cs ^ 1), true);
+        resolve();
+      } else {
+        nxt_ready = nq > 0;
+      }
+    };
     // K (S waves) and V (dP waves) rows of the first item into LDS: K into the
     // hand-over slots, V into the stage of the item's third tile (keys 0..63
     // in its Q part, 64..127 in its dO part); both areas are free until the
@@ -405,6 +424,7 @@ __global__ __launch_bounds__(QTHREADS) void attn_dkdv_queue_kernel(BwdArgs a, in
       // second, so the next item is taken before step ntiles - 2.
       const int nmain = ntiles >= 2 ? ntiles - 2 : 0;
       const bool need_next = !nxt_ready;
+      const bool early = need_next && nmain >= 1;  // the next item is published before a step's barrier
       walk_from(cur, 2, st0 + 2 >= QNST ? st0 + 2 - QNST : st0 + 2);
       // Copies of the last two steps: the next item's tiles 0 and 1.
       auto issue_peeled = [&](int t) {
@@ -490,7 +510,8 @@ __global__ __launch_bounds__(QTHREADS) void attn_dkdv_queue_kernel(BwdArgs a, in
           issue_next(nq, qt_begin);
           step(j);
         }
-        if (need_next) resolve();
+        if (early) collect();
+        else if (need_next) resolve();
         if (ntiles >= 2) {
           issue_peeled(0);
           step(ntiles - 2);
@@ -537,19 +558,27 @@ __global__ __launch_bounds__(QTHREADS) void attn_dkdv_queue_kernel(BwdArgs a, in
           wait_vmem();  // the tile issued above is read from the next step on
           __syncthreads();
         };
-        // The taker sends the queue's atomic two steps before the item is
-        // taken, between two runs of the same loop (no test inside it).
-        const int nbefore = need_next && nmain >= 2 ? nmain - 2 : 0;
+        // The taker sends the queue's atomic two steps before it publishes the
+        // next item, and publishes it before the barrier of the last main
+        // step; all between runs of the same loop (no test inside it).
+        const int npub = early ? nmain - 1 : nmain;
+        const int nbefore = early ? (npub >= 2 ? npub - 2 : 0) : (need_next && nmain >= 2 ? nmain - 2 : 0);
         for (int j = 0; j < nbefore; ++j) {
           issue_next(nq, qt_begin);
           step(j);
         }
         if (need_next && tid == kTaker) take_begin();
-        for (int j = nbefore; j < nmain; ++j) {
+        for (int j = nbefore; j < npub; ++j) {
           issue_next(nq, qt_begin);
           step(j);
         }
-        if (need_next) resolve();
+        if (early && tid == kTaker) publish();
+        for (int j = npub; j < nmain; ++j) {
+          issue_next(nq, qt_begin);
+          step(j);
+        }
+        if (early) collect();
+        else if (need_next) resolve();
         if (ntiles >= 2) {
           issue_peeled(0);
           step(ntiles - 2);
