@@ -158,3 +158,20 @@ def test_dkdv_pass_repeats_and_graph_replays(case):
         torch.cuda.synchronize()
         for got, ref in zip(out, (dq_ref, dk_ref, dv_ref)):
             assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("case", [
+    # 512 one-tile items (64 query rows, one query head per KV head) for 256
+    # persistent workgroups: each workgroup chains several, and every item's
+    # second tile is the next item's first.
+    Case("queue_d128_one_tile_items", 64, 64, 64, 8, 8, 128, workload_id=134),
+    # 480 items of 1, 3 and 5 tiles (causal, three 128-key tiles per head),
+    # KV lengths that leave whole items empty in some batches.
+    Case("queue_d128_mixed_item_lengths", 40, 300, 300, 4, 4, 128, causal=True,
+         kv_lens=tuple((300, 60, 0, 211, 129)[b % 5] for b in range(40)), workload_id=135),
+], ids=lambda c: c.name)
+def test_dkdv_queue_item_mixes(case):
+    """The head_dim-128 dK/dV workgroups take more items than there are
+    workgroups: one-tile items, empty items and items of different lengths
+    follow each other in one workgroup's stream of tiles."""
+    check_bwd(case)
