@@ -402,6 +402,10 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
       va[m] = lds_read16(vl + nrm[m]);
     }
     f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    // At head_dim 64 the row products run at raised wave priority: the wave
+    // that gets to them first keeps the matrix core while its partner works
+    // through its softmax (3-4% faster at B4 H8 T4096; slower at 128).
+    if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < C::KS; ++t) {
       s = mfma_bf16(ka[t % C::R], qf[t], s);
@@ -411,6 +415,7 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
         va[t % C::R] = lds_read16(vl + nrm[t + C::R]);
       }
     }
+    if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
     u32x2_t kt[1][C::DB][2];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
