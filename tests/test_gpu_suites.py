@@ -57,27 +57,35 @@ def test_gqa_suite_native_equals_repeated_kv():
         assert err <= TOL["bf16"], f"{name}: {err:.3e}"
 
 
-@pytest.mark.parametrize("key", [(8, 4096, 8), (8, 4096, 32), (1, 65536, 8)], ids=lambda k: f"B{k[0]}_kv{k[1]}_hkv{k[2]}")
+# Every batch-1 shape of the decode suite, and batch 8 at 4096 keys, against
+# the oracle on the whole output.
+DIRECT = [k for k in sorted(DECODE) if k[0] == 1] + [(8, 4096, 8), (8, 4096, 32)]
+
+
+@pytest.mark.parametrize("key", DIRECT, ids=lambda k: f"B{k[0]}_kv{k[1]}_hkv{k[2]}")
 def test_decode_suite(key):
     check_decode(DECODE[key])
 
 
-@pytest.mark.parametrize("hkv", [8, 32])
-def test_decode_suite_peak_point_B8_64k_keys(hkv):
-    """The pages' decode peak point: batch 8, 64k keys, 32 query heads, one
-    query each, full caches ("Attention performance", section
-    "Grouped-query attention and decoding"; the pages ran it with 8 KV heads).
-    Two seeded batches are repeated along the batch axis on the device, so the
-    host holds the oracle's inputs for two batches only; those two are checked
-    against the oracle, and every batch must equal its source bit for bit
-    (equal lengths give every batch the same key ranges and merge order)."""
+@pytest.mark.parametrize("n,hkv", [(16384, 8), (16384, 32), (65536, 8), (65536, 32)],
+                         ids=lambda v: str(v))
+def test_decode_suite_batch8_repeated(n, hkv):
+    """Batch 8 of the decode suite at 16k and 64k keys, 32 query heads, one
+    query each, full caches; 64k keys with 8 KV heads is the pages' decode
+    peak point ("Attention performance", section "Grouped-query attention and
+    decoding"). Two seeded batches are repeated along the batch axis on the
+    device, so the host holds the oracle's inputs for two batches only; those
+    two are checked against the oracle, and every batch must equal its source
+    bit for bit (equal lengths give every batch the same key ranges and merge
+    order)."""
     import torch
     from forward_backward_amd import attn
     from forward_backward_amd.inputs import Case
-    src = Case(f"dec_peak_src_hkv{hkv}", 2, 1, 65536, 32, hkv, 128, workload_id=610 + hkv, decode=True)
+    wid = (610 if n == 65536 else 650) + hkv
+    src = Case(f"dec_b8_src_kv{n}_hkv{hkv}", 2, 1, n, 32, hkv, 128, workload_id=wid, decode=True)
     host, dev, f64 = device_inputs(src, with_do=False)
     B = 8
-    print(f"[decode peak point] B{B} keys {src.Tkv} Hkv {hkv}", flush=True)
+    print(f"[decode batch 8, repeated sources] B{B} keys {src.Tkv} Hkv {hkv}", flush=True)
     idx = torch.arange(B, device="cuda") % src.B
     q, k, v = (torch.index_select(dev[n], 0, idx).contiguous() for n in ("q", "k", "v"))
     o, lse = attn.decode(q, k, v, scale=src.scale)
