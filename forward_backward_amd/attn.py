@@ -18,6 +18,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libattn_debug.so")  # the same library with address checks
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 ATTN_BF16, ATTN_FP32 = 0, 1
@@ -67,23 +68,41 @@ _SIGS = {
     "attn_decode_noalloc": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_int32, _V]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_last_error": (ctypes.c_char_p, []),
+    "attn_debug_take": (ctypes.c_int, [ctypes.POINTER(ctypes.c_ulonglong)]),
+    "attn_debug_selftest": (ctypes.c_int, [ctypes.c_void_p]),
 }
 EXPORTS = tuple(_SIGS)
+
+
+def load_library(path: str):
+    """A handle on a built library at `path`, with every entry point's signature set."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m forward_backward_amd.build`")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
 
 
 def lib(path: str = LIB_PATH):
     """Load libattn.so once; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(path):
-            raise RuntimeError(f"{path} is missing: build it with `python -m forward_backward_amd.build`")
-        handle = ctypes.CDLL(path)
-        for name, (res, args) in _SIGS.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load_library(path)
     return _lib
+
+
+def debug_take(handle=None):
+    """(accesses outside the registered buffers, first such address) since the
+    last call, from a library built with address checks (libattn_debug.so)."""
+    out = (ctypes.c_ulonglong * 2)()
+    L = handle if handle is not None else lib()
+    status = L.attn_debug_take(out)
+    if status != ATTN_OK:
+        raise AttnError(status, f"{L.attn_status_string(status).decode()}: {L.attn_last_error().decode()}")
+    return int(out[0]), int(out[1])
 
 
 def _check(status: int):

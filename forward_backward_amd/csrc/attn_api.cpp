@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "attn_internal.h"
 
@@ -57,7 +58,98 @@ size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
 }  // namespace
 
+namespace attn {
+// Setters and readers of the debug build's per-code-object address tables
+// (see attn_internal.h); a release build registers none.
+namespace {
+struct DbgRegistry {
+  DbgSetFn set[32];
+  DbgTakeFn take[32];
+  int n = 0;
+};
+DbgRegistry& dbg_registry() {
+  static DbgRegistry r;
+  return r;
+}
+}  // namespace
+int dbg_register(DbgSetFn set, DbgTakeFn take) {
+  DbgRegistry& r = dbg_registry();
+  if (r.n < 32) {
+    r.set[r.n] = set;
+    r.take[r.n] = take;
+    ++r.n;
+  }
+  return r.n;
+}
+}  // namespace attn
+
+namespace {
+// Debug build: register the byte ranges of a call's buffers with every code
+// object before its launches (nothing in a release build). The tables are
+// written synchronously once the stream's earlier work is done, so debug
+// calls run one at a time and cannot be captured into a graph.
+struct Buf {
+  const void* p;
+  size_t bytes;
+};
+attn_status_t dbg_prepare(std::initializer_list<Buf> bufs, void* stream) {
+#ifdef ATTN_DEBUG
+  attn::DbgRange r[attn::kDbgRanges];
+  int n = 0;
+  for (const Buf& b : bufs)
+    if (b.p != nullptr && b.bytes > 0 && n < attn::kDbgRanges) {
+      const unsigned long long lo = reinterpret_cast<unsigned long long>(b.p);
+      r[n++] = attn::DbgRange{lo, lo + b.bytes};
+    }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return fail(ATTN_ERR_UNSUPPORTED, "the debug build cannot be captured into a graph");
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(ATTN_ERR_HIP, "stream synchronisation failed");
+  const attn::DbgRegistry& reg = attn::dbg_registry();
+  for (int i = 0; i < reg.n; ++i)
+    if (reg.set[i](r, n) != hipSuccess) return fail(ATTN_ERR_HIP, "debug address table upload failed");
+#else
+  (void)bufs;
+  (void)stream;
+#endif
+  return ATTN_OK;
+}
+}  // namespace
+
 extern "C" {
+
+attn_status_t attn_debug_take(unsigned long long* out) {
+#ifdef ATTN_DEBUG
+  if (out == nullptr) return fail(ATTN_ERR_INVALID, "out must hold two values");
+  if (hipDeviceSynchronize() != hipSuccess) return fail(ATTN_ERR_HIP, "device synchronisation failed");
+  unsigned long long count = 0, first = 0;
+  const attn::DbgRegistry& reg = attn::dbg_registry();
+  for (int i = 0; i < reg.n; ++i)
+    if (reg.take[i](&count, &first) != hipSuccess) return fail(ATTN_ERR_HIP, "debug counter read failed");
+  out[0] = count;
+  out[1] = first;
+  return ok();
+#else
+  (void)out;
+  return fail(ATTN_ERR_UNSUPPORTED, "address checks are compiled into libattn_debug.so only");
+#endif
+}
+
+attn_status_t attn_debug_selftest(void* stream) {
+#ifdef ATTN_DEBUG
+  // A made-up address range: the self-test kernel only compares addresses.
+  const void* base = reinterpret_cast<const void*>(static_cast<uintptr_t>(1) << 40);
+  const attn_status_t st = dbg_prepare({{base, 32 * 16}}, stream);
+  if (st != ATTN_OK) return st;
+  if (attn::launch_debug_selftest(base, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(ATTN_ERR_HIP, "self-test launch failed");
+  return ok();
+#else
+  (void)stream;
+  return fail(ATTN_ERR_UNSUPPORTED, "address checks are compiled into libattn_debug.so only");
+#endif
+}
 
 attn_status_t attn_validate(const attn_params_t* p, int32_t op) {
   if (p == nullptr) return fail(ATTN_ERR_INVALID, "params is NULL");
@@ -153,6 +245,11 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
   hipError_t e;
   a.num_qtiles = (p->Tq + attn::kFwdBlockM - 1) / attn::kFwdBlockM;
   if ((long)a.num_qtiles * a.Hq * a.B >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "grid too large");
+  const size_t es = p->dtype == ATTN_BF16 ? 2 : 4;
+  st = dbg_prepare({{q, n.q * es}, {k, n.kv * es}, {v, n.kv * es}, {o, n.q * es}, {lse, n.stat * sizeof(float)},
+                    {p->kv_lens, p->B * sizeof(int32_t)}},
+                   stream);
+  if (st != ATTN_OK) return st;
   if (p->dtype == ATTN_BF16)
     e = attn::launch_fwd_bf16(a, p->D, s);
   else
@@ -192,6 +289,14 @@ attn_status_t bwd_setup(const attn_params_t* p, attn::BwdArgs& a, const void* ws
 }
 
 attn_status_t run_pass(const attn_params_t* p, const attn::BwdArgs& a, int pass, void* stream) {
+  const Sizes n = sizes_of(p);
+  const size_t es = p->dtype == ATTN_BF16 ? 2 : 4;
+  const attn_status_t st =
+      dbg_prepare({{a.q, n.q * es}, {a.k, n.kv * es}, {a.v, n.kv * es}, {a.o, n.q * es}, {a.dout, n.q * es},
+                   {a.dq, n.q * es}, {a.dk, n.kv * es}, {a.dv, n.kv * es}, {a.lse, n.stat * sizeof(float)},
+                   {a.delta, attn_bwd_workspace_size(p)}, {p->kv_lens, p->B * sizeof(int32_t)}},
+                  stream);
+  if (st != ATTN_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = p->dtype == ATTN_BF16 ? attn::launch_bwd_pass_bf16(a, p->D, pass, s)
                                        : attn::launch_bwd_pass_fp32(a, p->D, pass, s);
@@ -326,6 +431,13 @@ attn_status_t decode_run(const attn_params_t* p, const void* q, const void* k_ca
   a.budget = num_splits;
   a.num_rblocks = (int)decode_row_blocks(p);
   a.num_slots = (int)(num_splits + segs);
+  const Sizes n = sizes_of(p);
+  const attn_status_t st =
+      dbg_prepare({{q, n.q * size_t{2}}, {k_cache, n.kv * size_t{2}}, {v_cache, n.kv * size_t{2}}, {o, n.q * size_t{2}},
+                   {lse, n.stat * sizeof(float)}, {workspace, attn_decode_workspace_size(p, num_splits)},
+                   {p->kv_lens, p->B * sizeof(int32_t)}},
+                  stream);
+  if (st != ATTN_OK) return st;
   hipError_t e = attn::launch_decode_bf16(a, p->D, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "launch failed (hip error %d)", (int)e);
   return ok();

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_internal.h"
+
 namespace attn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -51,9 +53,49 @@ __device__ __forceinline__ u32x2_t lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
+#ifdef ATTN_DEBUG
+// Debug build: this code object's table of valid byte ranges and its counters
+// (accesses outside every range, the first such address). The host fills the
+// table before each call's launches and reads the counters through the
+// functions registered below (see attn_internal.h).
+namespace dbg {
+static __device__ DbgRange ranges[kDbgRanges];
+static __device__ int nranges;
+static __device__ unsigned long long counts[2];
+__device__ __forceinline__ void check(const void* p, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(p);
+  if (!dbg_in_ranges(a, bytes, ranges, nranges)) {
+    atomicAdd(&counts[0], 1ull);
+    atomicCAS(&counts[1], 0ull, a);
+  }
+}
+static hipError_t set(const DbgRange* r, int n) {
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(ranges), r, sizeof(DbgRange) * n, 0, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(nranges), &n, sizeof(int), 0, hipMemcpyHostToDevice);
+  return e;
+}
+static hipError_t take(unsigned long long* count, unsigned long long* first) {
+  unsigned long long c[2] = {0, 0};
+  hipError_t e = hipMemcpyFromSymbol(c, HIP_SYMBOL(counts), sizeof(c), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  *count += c[0];
+  if (*first == 0) *first = c[1];
+  const unsigned long long z[2] = {0, 0};
+  return hipMemcpyToSymbol(HIP_SYMBOL(counts), z, sizeof(z), 0, hipMemcpyHostToDevice);
+}
+static const int registered = dbg_register(&set, &take);
+}  // namespace dbg
+#define ATTN_DBG_CHECK(p, bytes) ::attn::dbg::check((p), (bytes))
+#else
+#define ATTN_DBG_CHECK(p, bytes) ((void)0)
+#endif
+
 __device__ __forceinline__ u32x4_t lds_read16(const uint16_t* p) { return *(const u32x4_t*)(p); }
 __device__ __forceinline__ void lds_write16(uint16_t* p, u32x4_t v) { *(u32x4_t*)(p) = v; }
-__device__ __forceinline__ u32x4_t gload16(const uint16_t* p) { return *(const u32x4_t*)(p); }
+__device__ __forceinline__ u32x4_t gload16(const uint16_t* p) {
+  ATTN_DBG_CHECK(p, 16);
+  return *(const u32x4_t*)(p);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -118,6 +160,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // expects it to change); the LDS address must be wave-uniform and is moved
 // into a scalar register first.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  ATTN_DBG_CHECK(g, 16);
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
@@ -131,6 +174,7 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
       : "memory");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  ATTN_DBG_CHECK(g, 4);
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
   asm volatile(
@@ -200,8 +244,10 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long
     const int r = Gm::row(i, wave, lane);
     const uint16_t* src = g + Gm::elem(Gm::clamp_row(r0, r, rlim), r, lane, rs);
     uint16_t* dst = tile + Gm::block(i, wave) * 512;
-    if constexpr (VISIBLE)
+    if constexpr (VISIBLE) {
+      ATTN_DBG_CHECK(src, 16);
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)dst, 16, 0, 0);
+    }
     else
       dma16(src, lds_addr(dst));
   }
@@ -218,6 +264,7 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
   const void* sbase = reinterpret_cast<const void*>(join_halves(lo, hi));
+  ATTN_DBG_CHECK(static_cast<const char*>(sbase) + voff, 16);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -257,6 +304,13 @@ __device__ __forceinline__ void dma16_batch(const void* base_a, const void* base
     return reinterpret_cast<const void*>(join_halves(lo, hi));
   };
   const void* sa = uniform(base_a);
+#ifdef ATTN_DEBUG
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    ATTN_DBG_CHECK(static_cast<const char*>(sa) + voff[i], 16);
+    if constexpr (TWO) ATTN_DBG_CHECK(static_cast<const char*>(uniform(base_b)) + voff[i], 16);
+  }
+#endif
   const uint32_t l0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
   uint32_t saved;
   if constexpr (ITERS == 2 && !TWO) {
@@ -344,9 +398,11 @@ struct TileCopy {
   __device__ __forceinline__ void copy_visible(uint16_t* tile, const uint16_t* g, long rs, int r0) const {
     const char* base = (const char*)(g + (long)r0 * rs);
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i)
+    for (int i = 0; i < ITERS; ++i) {
+      ATTN_DBG_CHECK(base + voff[i], 16);
       __builtin_amdgcn_global_load_lds((const void*)(base + voff[i]),
                                        (lds_void_t*)((char*)tile + lds_wave + i * WAVES * 1024), 16, 0, 0);
+    }
   }
 };
 

@@ -92,4 +92,26 @@ constexpr int kDecodeTileN = 64;  // keys per decode iteration
 constexpr int kDecodeRows = 64;   // packed query rows per decode workgroup
 constexpr int kDecodeSlots = 256; // decode workgroups resident at once (one per compute unit)
 
+// Address checks of the debug build (compiled with -DATTN_DEBUG into
+// libattn_debug.so): before a call's launches the host registers the byte
+// ranges of the call's buffers, and every global load and global->LDS copy
+// of the kernels checks the bytes it reads against them, counting the
+// accesses that fall outside (no trap: the kernels run on). Each code object
+// (source file) holds its own table and counters; each registers a setter
+// and a reader with the host side at load time.
+struct DbgRange {
+  unsigned long long lo, hi;  // bytes [lo, hi)
+};
+constexpr int kDbgRanges = 16;
+__host__ __device__ inline bool dbg_in_ranges(unsigned long long addr, unsigned bytes, const DbgRange* r, int n) {
+  for (int i = 0; i < n; ++i)
+    if (addr >= r[i].lo && addr <= r[i].hi && bytes <= r[i].hi - addr) return true;
+  return false;
+}
+using DbgSetFn = hipError_t (*)(const DbgRange* ranges, int n);
+using DbgTakeFn = hipError_t (*)(unsigned long long* count, unsigned long long* first);
+int dbg_register(DbgSetFn set, DbgTakeFn take);
+// One wave checking the 16-byte accesses at base + 16 * lane (64 lanes) without reading them.
+hipError_t launch_debug_selftest(const void* base, hipStream_t s);
+
 }  // namespace attn

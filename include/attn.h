@@ -205,6 +205,29 @@ const char* attn_status_string(attn_status_t status);
 /* Thread-local detail of the last failed call on this thread ("" if none). */
 const char* attn_last_error(void);
 
+/* Address checks of the debug build, for callers hunting a memory error, not
+ * for production use. libattn_debug.so (built from the same sources with
+ * -DATTN_DEBUG) registers the byte ranges of each call's buffers before its
+ * launches (tensors at their sizes from the parameters, the workspace at the
+ * size the call needs) and has every global load and global->LDS copy of the
+ * kernels check the bytes it reads against them. An access outside every
+ * range is counted and the kernel runs on. Debug calls synchronise their
+ * stream before launching and cannot be captured into a graph
+ * (ATTN_ERR_UNSUPPORTED).
+ * attn_debug_take synchronises the device and writes to out[0] the number of
+ * lane accesses found outside the ranges since its previous call and to
+ * out[1] the first such address (0 if none), then resets both. out must hold
+ * two values (caller-owned host memory). A release build (libattn.so)
+ * returns ATTN_ERR_UNSUPPORTED and leaves out untouched. */
+attn_status_t attn_debug_take(unsigned long long* out);
+
+/* Positive control of the debug build's checks: registers a made-up 512-byte
+ * range and launches one wave on `stream` whose 64 lanes check the 16-byte
+ * accesses at 16-byte steps from its start without reading any memory, so
+ * that the next attn_debug_take counts exactly 32 accesses outside it. A
+ * release build returns ATTN_ERR_UNSUPPORTED and launches nothing. */
+attn_status_t attn_debug_selftest(void* stream);
+
 #ifdef __cplusplus
 }
 #endif

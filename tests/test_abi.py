@@ -23,10 +23,26 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert "attn_fwd" in names and "attn_bwd" in names and "attn_decode" in names
-    lib = ctypes.CDLL(attn.LIB_PATH)
-    for n in names:
-        assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
+    for path in (attn.LIB_PATH, attn.DEBUG_LIB_PATH):
+        if not os.path.exists(path):
+            assert path == attn.DEBUG_LIB_PATH, f"{path} not built"
+            continue
+        lib = ctypes.CDLL(path)
+        for n in names:
+            assert hasattr(lib, n), f"{n} declared in attn.h but not exported by {os.path.basename(path)}"
     assert set(names) == set(attn.EXPORTS)
+
+
+def test_release_library_has_no_address_checks():
+    """attn_debug_take belongs to the debug build: the release library says so
+    without touching a device or the output."""
+    out = (ctypes.c_ulonglong * 2)(7, 9)
+    assert attn.lib().attn_debug_take(out) == attn.ATTN_ERR_UNSUPPORTED
+    assert b"libattn_debug.so" in attn.lib().attn_last_error()
+    assert (out[0], out[1]) == (7, 9)
+    with pytest.raises(attn.AttnError):
+        attn.debug_take()
+    assert attn.lib().attn_debug_selftest(None) == attn.ATTN_ERR_UNSUPPORTED
 
 
 def P(**kw):
