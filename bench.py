@@ -42,7 +42,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SYMBOLS = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_preprocess": "attn_delta_kernel",
+KERNEL_SYMBOLS = {"attn_fwd": "attn_fwd_bf16_kernel",
                   "bwd_dkdv": "attn_dkdv_queue_kernel", "bwd_dq": "attn_dq_pair_kernel",
                   "decode_split": "attn_decode_split_kernel", "decode_combine": "attn_decode_combine_kernel"}
 
@@ -409,33 +409,33 @@ def time_train_steps(case, steps, warmup, spread=False):
     ws = attn.bwd_workspace(q, k, case.causal, kv)
     kw = dict(scale=case.scale, causal=case.causal, kv_lens=kv, window=case.window)
 
+    # The passes attn_bwd runs, in its order: dQ with the preprocess outputs
+    # (D formed in the dQ kernel at bf16 head_dim 64/128), then dK/dV.
     def step(ev=None):
         attn.fwd(q, k, v, out=o, lse=lse, **kw)
         if ev: ev[1].record()
-        attn.bwd_preprocess(o, lse, do, ws, q, k, **kw)
+        attn.bwd_dq_and_preprocess(q, k, v, o, lse, do, ws, dq, **kw)
         if ev: ev[2].record()
         attn.bwd_dkdv(q, k, v, lse, do, ws, dk, dv, **kw)
         if ev: ev[3].record()
-        attn.bwd_dq(q, k, v, lse, do, ws, dq, **kw)
-        if ev: ev[4].record()
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         evs[i][0].record()
         step(evs[i])
     torch.cuda.synchronize()
-    total = evs[0][0].elapsed_time(evs[-1][4])
-    names = ["attn_fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    total = evs[0][0].elapsed_time(evs[-1][3])
+    names = ["attn_fwd", "bwd_dq", "bwd_dkdv"]
     per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
     if not torch.isfinite(dq.float()).all() or not torch.isfinite(o.float()).all():
         raise RuntimeError("non-finite outputs in the benchmark step")
     if not spread:
         return total / steps, per
-    dist = {"step_ms": quartiles([e[0].elapsed_time(e[4]) for e in evs]),
+    dist = {"step_ms": quartiles([e[0].elapsed_time(e[3]) for e in evs]),
             "per_kernel_ms": {n: quartiles([e[j].elapsed_time(e[j + 1]) for e in evs]) for j, n in enumerate(names)}}
     return total / steps, per, dist
 

@@ -62,6 +62,7 @@ _SIGS = {
     "attn_bwd_preprocess": (ctypes.c_int, [_P, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "attn_bwd_dkdv": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "attn_bwd_dq": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "attn_bwd_dq_and_preprocess": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "attn_decode_num_splits": (ctypes.c_int32, [_P]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [_P, ctypes.c_int32]),
     "attn_decode": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, ctypes.c_int32, _V, ctypes.c_size_t, _V]),
@@ -264,6 +265,17 @@ def bwd_dq(q, k, v, lse, do, ws, dq, scale=None, causal=False, kv_lens=None, win
     nbytes = _workspace(ws, lib().attn_bwd_workspace_size(ctypes.byref(p)), q.device)
     _check(lib().attn_bwd_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(do), _ptr(dq), _ptr(ws),
                              nbytes, _stream()))
+
+
+def bwd_dq_and_preprocess(q, k, v, o, lse, do, ws, dq, scale=None, causal=False, kv_lens=None, window=None):
+    """dQ and the preprocess pass's workspace contents in one call (one launch at
+    bf16 head_dim 64/128); bwd_dkdv may follow it directly."""
+    p = _params_for(q, k, scale, causal, kv_lens, window)
+    _bwd_inputs(p, q, k, v=v, o=o, lse=lse, do=do)
+    _like("dq", dq, q.shape, q.dtype, q.device)
+    nbytes = _workspace(ws, lib().attn_bwd_workspace_size(ctypes.byref(p)), q.device)
+    _check(lib().attn_bwd_dq_and_preprocess(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                            _ptr(dq), _ptr(ws), nbytes, _stream()))
 
 
 def decode_workspace(q, k_cache, num_splits=0):

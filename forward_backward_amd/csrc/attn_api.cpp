@@ -348,6 +348,35 @@ attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, 
   return run_pass(p, a, attn::kBwdDq, stream);
 }
 
+// dQ together with the preprocess outputs: one launch where the dQ kernel
+// forms D itself (bf16 head_dim 64 and 128), else the pre-kernel and then dQ.
+// Without query rows the dQ grid is empty, and the pre-kernel (which always
+// launches) still zeroes the dK/dV pass's work counters.
+static attn_status_t dq_and_preprocess(const attn_params_t* p, attn::BwdArgs& a, void* stream) {
+  if (p->dtype == ATTN_BF16 && (p->D == 64 || p->D == 128) && (long)p->B * p->Hq * p->Tq > 0) {
+    a.dq_stats = 1;
+    const attn_status_t st = run_pass(p, a, attn::kBwdDq, stream);
+    a.dq_stats = 0;
+    return st;
+  }
+  const attn_status_t st = run_pass(p, a, attn::kBwdPre, stream);
+  return st != ATTN_OK ? st : run_pass(p, a, attn::kBwdDq, stream);
+}
+
+attn_status_t attn_bwd_dq_and_preprocess(const attn_params_t* p, const void* q, const void* k, const void* v,
+                                         const void* o, const float* lse, const void* dout, void* dq,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  attn::BwdArgs a;
+  attn_status_t st = bwd_setup(p, a, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  const Sizes n = sizes_of(p);
+  if (check_ptr(q, n.q, true) || check_ptr(k, n.kv, true) || check_ptr(v, n.kv, true) || check_ptr(o, n.q, true) ||
+      check_ptr(lse, n.stat, false) || check_ptr(dout, n.q, true) || check_ptr(dq, n.q, true))
+    return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq;
+  return dq_and_preprocess(p, a, stream);
+}
+
 attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                        size_t workspace_bytes, void* stream) {
@@ -360,11 +389,8 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
       check_ptr(dk, n.kv, true) || check_ptr(dv, n.kv, true))
     return fail(ATTN_ERR_INVALID, "tensor pointers must be non-NULL and 16-byte aligned (except empty tensors)");
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
-  for (int pass : {attn::kBwdPre, attn::kBwdDkdv, attn::kBwdDq}) {
-    st = run_pass(p, a, pass, stream);
-    if (st != ATTN_OK) return st;
-  }
-  return ok();
+  st = dq_and_preprocess(p, a, stream);
+  return st != ATTN_OK ? st : run_pass(p, a, attn::kBwdDkdv, stream);
 }
 
 // Packed query rows (Tq * G) of one (batch, KV head) in blocks of the decode tile.

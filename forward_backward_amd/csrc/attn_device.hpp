@@ -111,6 +111,49 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// Partial of D = rowsum(dO * O) over one lane's half of a bf16 row: the
+// 16-byte chunks t = 0 .. KS - 1 at elements 16 t + 8 hh .. + 7 (the layout of
+// the dQ kernel's Q/dO fragments), in one fixed chain of fused multiply-adds.
+// D is the sum of the two halves' partials. The dQ kernel and the head_dim
+// 64/128 pre-kernel both form D this way, so they agree bit for bit.
+template <int KS>
+__device__ __forceinline__ float row_dot_half(const u32x4_t (&o)[KS], const u32x4_t (&g)[KS]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = __builtin_fmaf(bf16_lo(o[t][w]), bf16_lo(g[t][w]), acc);
+      acc = __builtin_fmaf(bf16_hi(o[t][w]), bf16_hi(g[t][w]), acc);
+    }
+  return acc;
+}
+
+// Three bf16 terms whose sum is x to fp32 precision (each term is the
+// round-to-nearest-even bf16 of what the previous ones left; every
+// difference is exact in fp32).
+__device__ __forceinline__ u32x2_t split_bf16x3(float x) {
+  const float h = bf16_lo(pack_bf16(x, 0.f));
+  const float r1 = x - h;
+  const float m = bf16_lo(pack_bf16(r1, 0.f));
+  const float r2 = r1 - m;
+  return u32x2_t{pack_bf16(h, m), pack_bf16(r2, 0.f)};
+}
+
+// The backward's per-row statistics of row `st` ([B, Hq, Tq] index) from its
+// D = rowsum(dO * O) and LSE: D, the base-2 LSE (LSE * log2(e)) that the tile
+// kernels load, and the row terms the dK/dV kernel adds to S and dP with one
+// extra matrix k-step: -LSE/scale (so that scale * log2(e) * (S - LSE/scale)
+// is the base-2 exponent of P) and -D, each as three bf16 terms. Rows without
+// a finite LSE (no valid key) get 0 terms; no kernel forms P for them.
+__device__ __forceinline__ void write_row_stats(const BwdArgs& a, long st, float dsum, float lse) {
+  a.delta[st] = dsum;
+  a.lse2[st] = lse * 1.4426950408889634f;
+  const float x = __builtin_isfinite(lse) ? -lse / a.scale : 0.f;
+  const u32x2_t xs = split_bf16x3(x), ys = split_bf16x3(-dsum);
+  *(u32x4_t*)(a.rowstat + st * 8) = u32x4_t{xs[0], xs[1], ys[0], ys[1]};
+}
+
 // LDS bank model used for layouts (measured with the bank-conflict counter):
 // 64 banks of 4 bytes; a 128-bit read serves 16 lanes per cycle, the 64-bit
 // transpose read 32 lanes per cycle.

@@ -347,8 +347,25 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     gf[t] = row_ok ? gload16((const uint16_t*)a.dout + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
   }
   const long stat = ((long)b * a.Hq + h) * a.Tq + qrow;
-  const float lse2 = row_ok ? a.lse2[stat] : INFINITY;
-  const float dlt = row_ok ? a.delta[stat] : 0.f;
+  float lse2, dlt;
+  if (a.dq_stats) {
+    // D of the lane's row from its O and dO fragments (the pre-kernel's
+    // chain, so the same bits), and the statistics the dK/dV pass reads:
+    // written once per row, by the block-0 wave of the pair.
+    u32x4_t of[C::KS];
+#pragma unroll
+    for (int t = 0; t < C::KS; ++t)
+      of[t] = row_ok ? gload16((const uint16_t*)a.o + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    const float dsum = half_sum(row_dot_half<C::KS>(of, gf));
+    const float lse = row_ok ? a.lse[stat] : 0.f;
+    if (row_ok && half == 0 && hh == 0) write_row_stats(a, stat, dsum, lse);
+    lse2 = row_ok ? lse * 1.4426950408889634f : INFINITY;
+    dlt = row_ok ? dsum : 0.f;
+    if (blockIdx.x == 0 && tid < kBwdQueueWords && a.queue != nullptr) a.queue[tid] = 0u;
+  } else {
+    lse2 = row_ok ? a.lse2[stat] : INFINITY;
+    dlt = row_ok ? a.delta[stat] : 0.f;
+  }
   const float c = a.scale_log2;
 
   f32x16_t acc[C::DB];

@@ -886,23 +886,8 @@ __global__ __launch_bounds__(256, D > 64 ? 1 : 2) void attn_dkdv_f32_kernel(BwdA
   }
 }
 
-// Three bf16 terms whose sum is x to fp32 precision (each term is the
-// round-to-nearest-even bf16 of what the previous ones left; every
-// difference is exact in fp32).
-__device__ __forceinline__ u32x2_t split_bf16x3(float x) {
-  const float h = bf16_lo(pack_bf16(x, 0.f));
-  const float r1 = x - h;
-  const float m = bf16_lo(pack_bf16(r1, 0.f));
-  const float r2 = r1 - m;
-  return u32x2_t{pack_bf16(h, m), pack_bf16(r2, 0.f)};
-}
-
-// D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32, the base-2 LSE
-// (LSE * log2(e)) that the tile kernels load straight into LDS, and the row
-// terms the dK/dV kernel adds to S and dP with one extra matrix k-step:
-// -LSE/scale (so that scale * log2(e) * (S - LSE/scale) is the base-2
-// exponent of P) and -D, each as three bf16 terms. Rows without a finite LSE
-// (no valid key) get 0; no kernel forms P for them.
+// D[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d] in fp32 and the other
+// per-row statistics of write_row_stats (head_dim 32 and 256, and fp32).
 // Each thread reduces 8 contiguous elements; D/8 threads share a row.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void attn_delta_kernel(BwdArgs a, long rows) {
@@ -937,18 +922,53 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(BwdArgs a, long rows) {
     const int i = (int)((row / a.Hq) % a.Tq);
     const int b = (int)(row / ((long)a.Hq * a.Tq));
     const long st = ((long)b * a.Hq + h) * a.Tq + i;
-    a.delta[st] = acc;
-    const float lse = a.lse[st];
-    a.lse2[st] = lse * 1.4426950408889634f;
-    const float x = __builtin_isfinite(lse) ? -lse / a.scale : 0.f;
-    const u32x2_t xs = split_bf16x3(x), ys = split_bf16x3(-acc);
-    *(u32x4_t*)(a.rowstat + st * 8) = u32x4_t{xs[0], xs[1], ys[0], ys[1]};
+    write_row_stats(a, st, acc, a.lse[st]);
+  }
+}
+
+// The same statistics at bf16 head_dim 64 and 128, with D formed as the dQ
+// kernel forms it (row_dot_half: two threads per row, each one chain over its
+// half of the row), so that the dQ pass that computes them itself
+// (attn_bwd_dq_and_preprocess) writes the same bits.
+template <int D>
+__global__ __launch_bounds__(256) void attn_delta_rows_kernel(BwdArgs a, long rows) {
+  constexpr int KS = D / 16;
+  const long gt = (long)blockIdx.x * 256 + threadIdx.x;
+  // The work counters of the dK/dV pass start at zero.
+  if (blockIdx.x == 0 && threadIdx.x < kBwdQueueWords && a.queue != nullptr) a.queue[threadIdx.x] = 0u;
+  const long row = gt >> 1;  // row index in [B, Tq, Hq] order
+  const int hh = (int)(gt & 1);
+  float p = 0.f;
+  if (row < rows) {
+    const uint16_t* o = (const uint16_t*)a.o + row * D + 8 * hh;
+    const uint16_t* g = (const uint16_t*)a.dout + row * D + 8 * hh;
+    u32x4_t of[KS], gf[KS];
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      of[t] = gload16(o + 16 * t);
+      gf[t] = gload16(g + 16 * t);
+    }
+    p = row_dot_half<KS>(of, gf);
+  }
+  const float dsum = p + __shfl_xor(p, 1, 64);
+  if (row < rows && hh == 0) {
+    const int h = (int)(row % a.Hq);
+    const int i = (int)((row / a.Hq) % a.Tq);
+    const int b = (int)(row / ((long)a.Hq * a.Tq));
+    const long st = ((long)b * a.Hq + h) * a.Tq + i;
+    write_row_stats(a, st, dsum, a.lse[st]);
   }
 }
 
 template <int D>
 void launch_delta(const BwdArgs& a, bool bf16, hipStream_t s) {
   const long rows = (long)a.B * a.Tq * a.Hq;
+  if (bf16 && (D == 64 || D == 128)) {
+    const long threads = rows * 2;
+    const unsigned blocks = threads > 0 ? (unsigned)((threads + 255) / 256) : 1u;
+    hipLaunchKernelGGL((attn_delta_rows_kernel<D == 64 ? 64 : 128>), dim3(blocks), dim3(256), 0, s, a, rows);
+    return;
+  }
   const long threads = rows * (D / 8);
   const unsigned blocks = threads > 0 ? (unsigned)((threads + 255) / 256) : 1u;  // one block zeroes the counters
   if (bf16)

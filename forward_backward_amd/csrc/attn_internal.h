@@ -49,6 +49,8 @@ struct BwdArgs {
   int heads_per_split;
   float* dkv_part;         // workspace when kv_split > 1: fp32 partial dK then dV, [kv_split][B, Tkv, Hkv, D] each
   unsigned* queue;         // workspace: kBwdQueueWords work counters, zero between passes
+  int dq_stats;            // dQ pass (bf16 head_dim 64/128): form D from O and dO itself, write the
+                           // pre-kernel's statistics and zero the counters (attn_bwd_dq_and_preprocess)
 };
 
 // Arguments of the split-KV decode kernels.

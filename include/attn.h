@@ -108,7 +108,8 @@ attn_status_t attn_fwd(const attn_params_t* p, const void* q, const void* k, con
  * a reduction pass; S depends only on the shape, so results stay bitwise
  * reproducible. The last 256 bytes hold the work counters of the head_dim 128
  * dK/dV pass (persistent workgroups taking 128-key tiles from a queue): the
- * preprocess pass sets them to zero and the dK/dV pass leaves them at zero. */
+ * preprocess (or attn_bwd_dq_and_preprocess) sets them to zero and the dK/dV
+ * pass leaves them at zero. */
 size_t attn_bwd_workspace_size(const attn_params_t* p);
 
 /* Backward: the gradients of a scalar loss with respect to Q, K and V given
@@ -119,9 +120,11 @@ size_t attn_bwd_workspace_size(const attn_params_t* p);
  * "When to use which"; "H100 (Hopper)", section "Why", where it is the
  * robust choice). P is recomputed from the forward's `lse`, the residuals
  * being O and LSE only ("Attention performance", section "Memory").
- * A pre-kernel forms D = rowsum(dO * O) in the workspace; one kernel forms
- * dK and dV per KV tile (summing the G query heads of a group in a fixed
- * order); one kernel forms dQ per query tile.
+ * D = rowsum(dO * O) is formed first (by the dQ kernel itself at bf16
+ * head_dim 64 and 128, which then runs first; by a pre-kernel otherwise) and
+ * kept in the workspace; one kernel forms dK and dV per KV tile (summing the
+ * G query heads of a group in a fixed order); one kernel forms dQ per query
+ * tile. attn_bwd runs attn_bwd_dq_and_preprocess, then attn_bwd_dkdv.
  * q, k, v, o, lse as produced/consumed by attn_fwd; dout = dO like q.
  * dq like q; dk, dv like k. Keys at or past kv_lens[b] get dK = dV = 0.
  * Reruns on the same inputs are bitwise identical. */
@@ -129,15 +132,20 @@ attn_status_t attn_bwd(const attn_params_t* p, const void* q, const void* k, con
                        const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* The three passes of attn_bwd as separate calls, in the order attn_bwd
- * runs them (the split backward of "Attention performance", section "When
- * to use which"). attn_bwd_preprocess writes D = rowsum(dO * O) and LSE * log2(e)
- * into the workspace (and zeroes its work counters); attn_bwd_dkdv and
- * attn_bwd_dq read them and are independent of each other, so a caller may
- * run them on two streams once the preprocess has completed. attn_bwd_dkdv
- * also counts its work in the workspace's counters and returns them to zero,
- * so the same workspace serves the next pass or a replay of a captured graph;
- * two attn_bwd_dkdv calls must not run at the same time on one workspace.
+/* The passes of attn_bwd as separate calls (the split backward of
+ * "Attention performance", section "When to use which").
+ * attn_bwd_preprocess writes D = rowsum(dO * O) and LSE * log2(e) into the
+ * workspace (and zeroes its work counters); attn_bwd_dkdv and attn_bwd_dq
+ * read them and are independent of each other, so a caller may run them on
+ * two streams once the preprocess has completed. attn_bwd_dq_and_preprocess
+ * does what attn_bwd_preprocess and then attn_bwd_dq do, in one launch at
+ * bf16 head_dim 64 and 128 (the dQ kernel forms D from O and dO itself), and
+ * writes the same workspace bits, so attn_bwd_dkdv may follow it; attn_bwd is
+ * that call and then attn_bwd_dkdv. Every order gives the same gradients bit
+ * for bit. attn_bwd_dkdv also counts its work in the workspace's counters and
+ * returns them to zero, so the same workspace serves the next pass or a
+ * replay of a captured graph; two attn_bwd_dkdv calls must not run at the
+ * same time on one workspace, nor one with a preprocess on that workspace.
  * Arguments mean what they mean for attn_bwd. */
 attn_status_t attn_bwd_preprocess(const attn_params_t* p, const void* o, const float* lse, const void* dout,
                                   void* workspace, size_t workspace_bytes, void* stream);
@@ -146,6 +154,9 @@ attn_status_t attn_bwd_dkdv(const attn_params_t* p, const void* q, const void* k
                             void* stream);
 attn_status_t attn_bwd_dq(const attn_params_t* p, const void* q, const void* k, const void* v, const float* lse,
                           const void* dout, void* dq, const void* workspace, size_t workspace_bytes, void* stream);
+attn_status_t attn_bwd_dq_and_preprocess(const attn_params_t* p, const void* q, const void* k, const void* v,
+                                         const void* o, const float* lse, const void* dout, void* dq,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Split budget of the split-KV decode ("Attention performance", section
  * "Grouped-query attention and decoding", where the keys are split because
