@@ -134,6 +134,12 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.attn_bwd_dkdv(ctypes.byref(p), *([FAKE] * 6), None, FAKE, need, None) == attn.ATTN_ERR_INVALID
     assert L.attn_bwd_dq(ctypes.byref(p), *([FAKE] * 6), FAKE, need - 4, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd_dq(ctypes.byref(p), MISALIGNED, *([FAKE] * 5), FAKE, need, None) == attn.ATTN_ERR_INVALID
+    # dQ with the preprocess outputs: q, k, v, o, lse, dout, dq, then the workspace.
+    assert L.attn_bwd_dq_and_preprocess(ctypes.byref(p), *([FAKE] * 7), FAKE, need - 1, None) == \
+        attn.ATTN_ERR_WORKSPACE
+    assert L.attn_bwd_dq_and_preprocess(ctypes.byref(p), *([FAKE] * 3), None, *([FAKE] * 3), FAKE, need, None) == \
+        attn.ATTN_ERR_INVALID
+    assert L.attn_bwd_dq_and_preprocess(ctypes.byref(bad), *([FAKE] * 7), FAKE, need, None) == attn.ATTN_ERR_INVALID
     d = P(Tq=16, Tkv=16384, Hq=32, Hkv=8)
     s = L.attn_decode_num_splits(ctypes.byref(d))
     assert s >= 2
@@ -221,7 +227,8 @@ def test_binding_rejects_every_malformed_tensor_before_any_launch(host_binding):
                   lambda bl=bl: attn.bwd(q, k, v, o, bl, do),
                   lambda bl=bl: attn.bwd_preprocess(o, bl, do, ws, q, k),
                   lambda bl=bl: attn.bwd_dkdv(q, k, v, bl, do, ws, torch.zeros_like(k), torch.zeros_like(k)),
-                  lambda bl=bl: attn.bwd_dq(q, k, v, bl, do, ws, torch.zeros_like(q))]
+                  lambda bl=bl: attn.bwd_dq(q, k, v, bl, do, ws, torch.zeros_like(q)),
+                  lambda bl=bl: attn.bwd_dq_and_preprocess(q, k, v, o, bl, do, ws, torch.zeros_like(q))]
     for bq in bad_q_like:
         cases += [lambda bq=bq: attn.fwd(q, k, v, out=bq),
                   lambda bq=bq: attn.bwd(q, k, v, bq, lse, do),
@@ -229,7 +236,10 @@ def test_binding_rejects_every_malformed_tensor_before_any_launch(host_binding):
                   lambda bq=bq: attn.bwd_preprocess(bq, lse, do, ws, q, k),
                   lambda bq=bq: attn.bwd_preprocess(o, lse, bq, ws, q, k),
                   lambda bq=bq: attn.bwd_dq(q, k, v, lse, bq, ws, torch.zeros_like(q)),
-                  lambda bq=bq: attn.bwd_dq(q, k, v, lse, do, ws, bq)]
+                  lambda bq=bq: attn.bwd_dq(q, k, v, lse, do, ws, bq),
+                  lambda bq=bq: attn.bwd_dq_and_preprocess(q, k, v, bq, lse, do, ws, torch.zeros_like(q)),
+                  lambda bq=bq: attn.bwd_dq_and_preprocess(q, k, v, o, lse, bq, ws, torch.zeros_like(q)),
+                  lambda bq=bq: attn.bwd_dq_and_preprocess(q, k, v, o, lse, do, ws, bq)]
     for bk in bad_k_like:
         cases += [lambda bk=bk: attn.fwd(q, k, bk),
                   lambda bk=bk: attn.bwd(q, k, bk, o, lse, do),
@@ -237,12 +247,14 @@ def test_binding_rejects_every_malformed_tensor_before_any_launch(host_binding):
                   lambda bk=bk: attn.bwd_dkdv(q, k, v, lse, do, ws, bk, torch.zeros_like(k)),
                   lambda bk=bk: attn.bwd_dkdv(q, k, v, lse, do, ws, torch.zeros_like(k), bk),
                   lambda bk=bk: attn.bwd_dq(q, k, bk, lse, do, ws, torch.zeros_like(q)),
+                  lambda bk=bk: attn.bwd_dq_and_preprocess(q, k, bk, o, lse, do, ws, torch.zeros_like(q)),
                   lambda bk=bk: attn.decode(q, k, bk)]
     small_ws = ws[:-1]
     cases += [lambda: attn.bwd(q, k, v, o, lse, do, workspace=small_ws),
               lambda: attn.bwd_preprocess(o, lse, do, small_ws, q, k),
               lambda: attn.bwd_dkdv(q, k, v, lse, do, small_ws, torch.zeros_like(k), torch.zeros_like(k)),
               lambda: attn.bwd_dq(q, k, v, lse, do, small_ws, torch.zeros_like(q)),
+              lambda: attn.bwd_dq_and_preprocess(q, k, v, o, lse, do, small_ws, torch.zeros_like(q)),
               lambda: attn.bwd_dq(q, k, v, lse, do, ws[::2], torch.zeros_like(q)),
               lambda: attn.bwd_dq(q, k, v, lse, do, "not a tensor", torch.zeros_like(q)),
               lambda: attn.fwd(q, k, v, kv_lens=torch.zeros(2, dtype=torch.int64)),

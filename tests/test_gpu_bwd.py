@@ -175,3 +175,36 @@ def test_dkdv_queue_item_mixes(case):
     workgroups: one-tile items, empty items and items of different lengths
     follow each other in one workgroup's stream of tiles."""
     check_bwd(case)
+
+
+@pytest.mark.parametrize("case", [
+    Case("dqpre_d128_gqa_causal_kvlen", 2, 333, 333, 8, 2, 128, causal=True, kv_lens=(333, 0), workload_id=136),
+    Case("dqpre_d64_window_ragged", 2, 300, 300, 4, 4, 64, causal=True, window=(40, 0), workload_id=137),
+    Case("dqpre_d32_unfused", 1, 200, 200, 4, 2, 32, workload_id=138),
+], ids=lambda c: c.name)
+def test_dq_and_preprocess_writes_the_preprocess_bits(case):
+    """attn_bwd_dq_and_preprocess (at bf16 head_dim 64/128 one dQ launch that
+    forms D itself) leaves the same workspace statistics (D, LSE * log2(e),
+    the row terms) and the same dQ as the preprocess pass followed by dQ,
+    bit for bit, including rows with no valid key (LSE = -inf)."""
+    import torch
+    from forward_backward_amd import attn
+    host, dev, _ = device_inputs(case)
+    print(f"[dq and preprocess] {case.name}", flush=True)
+    kw = dict(scale=case.scale, causal=case.causal, kv_lens=dev["kv_lens"], window=case.window)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    o, lse = attn.fwd(q, k, v, **kw)
+    ws1 = attn.bwd_workspace(q, k, causal=case.causal, kv_lens=dev["kv_lens"], window=case.window)
+    ws2 = torch.full_like(ws1, 0x5A)
+    dq1, dq2 = torch.empty_like(q), torch.empty_like(q)
+    attn.bwd_preprocess(o, lse, do, ws1, q, k, **kw)
+    attn.bwd_dq(q, k, v, lse, do, ws1, dq1, **kw)
+    attn.bwd_dq_and_preprocess(q, k, v, o, lse, do, ws2, dq2, **kw)
+    torch.cuda.synchronize()
+    # Workspace layout: D and LSE * log2(e) (fp32 per row), then 16 bytes of
+    # row terms per row, each region starting on a 256-byte boundary.
+    rows = case.B * case.Hq * case.Tq
+    region = (rows * 4 + 255) // 256 * 256
+    for name, lo, n in (("D", 0, rows * 4), ("LSE * log2(e)", region, rows * 4), ("row terms", 2 * region, rows * 16)):
+        assert torch.equal(ws1[lo:lo + n], ws2[lo:lo + n]), name
+    assert torch.equal(dq1.view(torch.int16), dq2.view(torch.int16))
