@@ -1054,7 +1054,7 @@ def cpu_oracle_configs():
     f64 = {n: I.to_float64(host[n], c5.dtype) for n in ("q", "k", "v")}
     dec_ms = med3(lambda: oracle.attention_decode(f64["q"], f64["k"], f64["v"], c5.scale, host["kv_lens"])) * 1e3
     fl = effective_flops(c5.Hq, c5.Tq, host["kv_lens"], c5.D, "fwd")
-    rows.append({"workload": c5.name, "sample": "whole workload", "fwd_ms": round(dec_ms, 3),
+    rows.append({"workload": c5.name, "sample": "whole workload", "calls": 3, "fwd_ms": round(dec_ms, 3),
                  "fwd_gflops": round(fl / (dec_ms * 1e-3) / 1e9, 2)})
     log(f"  oracle per workload: {time.perf_counter() - t_start:.1f} s")
     return {"blas": blas, "threads": threads,
