@@ -247,7 +247,7 @@ def bwd_preprocess(o, lse, do, ws, q, k, scale=None, causal=False, kv_lens=None,
 
 
 def bwd_dkdv(q, k, v, lse, do, ws, dk, dv, scale=None, causal=False, kv_lens=None, window=None):
-    """Pass 2 of the backward: dK and dV (needs the preprocess pass done)."""
+    """Pass 2 of the backward: dK and dV (needs the preprocess pass, or bwd_dq_and_preprocess, done)."""
     p = _params_for(q, k, scale, causal, kv_lens, window)
     _bwd_inputs(p, q, k, v=v, lse=lse, do=do)
     _like("dk", dk, k.shape, k.dtype, q.device)
