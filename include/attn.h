@@ -61,7 +61,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, bad sizes, Hq % Hkv != 0, causal or window with Tq != Tkv,
                                causal or window in decode, bad scale */
-  ATTN_ERR_UNSUPPORTED = 2, /* head_dim or dtype this build has no kernel for: D outside {32, 64, 128, 256},
+  ATTN_ERR_UNSUPPORTED = 2, /* head_dim or dtype the library has no kernel for: D outside {32, 64, 128, 256},
                                fp32 with D = 256, fp32 decode; or a problem too large for one launch */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_size query */
   ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
