@@ -38,8 +38,11 @@
  *     to [0, Tkv] by the kernels (the host cannot read it without a sync).
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
  *     asynchronous on it. The library never allocates, frees or
- *     synchronises and is safe to call from several threads; its only state
- *     is the per-device address of attn_decode_noalloc's static scratch.
+ *     synchronises (the address-checking debug build at the end of this
+ *     header does synchronise) and is safe to call from several threads; its
+ *     only state is, per device, the address of attn_decode_noalloc's static
+ *     scratch and the compute-unit count that sizes the persistent dK/dV
+ *     grid.
  *   - Argument errors are reported before anything is launched: the call
  *     returns a status and attn_last_error() (thread-local) describes it.
  *     The pages' own rule is to reject what cannot be computed exactly
