@@ -439,6 +439,9 @@ attn_status_t decode_check(const attn_params_t* p, const void* q, const void* k_
   if (num_splits < 0) return fail(ATTN_ERR_INVALID, "num_splits must be >= 0 (0 = automatic)");
   if (num_splits == 0) num_splits = attn_decode_num_splits(p);
   if ((long)num_splits + decode_segments(p) >= kMaxGrid) return fail(ATTN_ERR_UNSUPPORTED, "too many splits");
+  // The kernels count the key tiles of all segments in 32 bits.
+  if ((double)decode_segments(p) * (double)((p->Tkv + attn::kDecodeTileN - 1) / attn::kDecodeTileN) >= 2147483648.0)
+    return fail(ATTN_ERR_UNSUPPORTED, "decode problem too large (key tiles of all segments must stay below 2^31)");
   need = attn_decode_workspace_size(p, num_splits);
   return ATTN_OK;
 }

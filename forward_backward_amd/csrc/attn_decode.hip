@@ -83,61 +83,74 @@ __device__ __forceinline__ int key_tiles(const DecodeArgs& a, int b) {
 }
 
 // Ranges of a segment with n tiles out of U in total: min(n, ceil(n * P / U)).
-__device__ __forceinline__ int num_ranges(int n, int P, long U) {
+__device__ __forceinline__ unsigned num_ranges(unsigned n, unsigned P, unsigned U) {
   if (n == 0) return 0;
-  const unsigned long num = (unsigned long)n * (unsigned)P + (unsigned long)(U - 1);
-  unsigned long k;
-  if ((num >> 32) == 0 && (U >> 32) == 0)
-    k = (unsigned)num / (unsigned)U;  // 32-bit division when the operands fit
-  else
-    k = num / (unsigned long)U;
-  return k < (unsigned long)n ? (int)k : n;
+  const unsigned long long num = (unsigned long long)n * P + (U - 1);
+  const unsigned long long k = (num >> 32) == 0 ? (unsigned)num / U : num / U;
+  return k < n ? (unsigned)k : n;
 }
 
-__device__ __forceinline__ long wave_sum(long x) {
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+// Inclusive sum over the 64 lanes of a wave (every lane active): sums within
+// each 16-lane row by shifts of 1, 2, 4 and 8 lanes, then the last lane of
+// rows 0 and 2 added to rows 1 and 3, and the last lane of row 1 to rows 2
+// and 3 (row broadcasts). Lanes whose source lies outside the row add 0.
+__device__ __forceinline__ unsigned wave_scan(unsigned v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return (unsigned)x;
 }
-
-__device__ __forceinline__ long wave_incl_scan(long x, int lane) {
-  for (int off = 1; off < 64; off <<= 1) {
-    const long y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  return x;
+__device__ __forceinline__ unsigned lane_value(unsigned x, int lane) {
+  return (unsigned)__builtin_amdgcn_readlane((int)x, lane);
 }
 
 // The schedule is evaluated by every wave on its own, lane i taking batch
-// b0 + i of each chunk of 64 batches, so its cost grows with B / 64.
+// b0 + i of each chunk of 64 batches, so its cost grows with B / 64. Counts
+// are 32-bit: the host bounds the key tiles of all segments below 2^31.
+// U: key tiles of all segments; P: the split budget.
+struct Sched {
+  unsigned U, P;
+};
 
-// U: key tiles of all segments.
-__device__ __forceinline__ long total_tiles(const DecodeArgs& a, int lane) {
-  long s = 0;
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int bb = b0 + lane;
-    s += wave_sum(bb < a.B ? key_tiles(a, bb) : 0);
-  }
-  return s * a.Hkv * a.num_rblocks;
+// Key tiles of batch b0 + lane (0 past the last batch).
+__device__ __forceinline__ unsigned chunk_tiles(const DecodeArgs& a, int b0, int lane) {
+  const int bb = b0 + lane;
+  return bb < a.B ? (unsigned)key_tiles(a, bb) : 0u;
 }
 
-// Batch b's first slot (ranges of earlier batches) and its ranges per segment.
-__device__ __forceinline__ void batch_slots(const DecodeArgs& a, long U, int b, int lane, long& first, int& k) {
-  long cum = 0;
+// n0: this lane's key tiles in the first chunk of batches.
+__device__ __forceinline__ Sched schedule(const DecodeArgs& a, unsigned n0, int lane) {
+  unsigned n_tot = lane_value(wave_scan(n0), 63);
+  for (int b0 = 64; b0 < a.B; b0 += 64) n_tot += lane_value(wave_scan(chunk_tiles(a, b0, lane)), 63);
+  Sched s;
+  s.U = n_tot * (unsigned)(a.Hkv * a.num_rblocks);
+  s.P = (unsigned)a.budget;
+  return s;
+}
+
+// Batch b's first slot (ranges of earlier batches) and its ranges per
+// segment; b may differ between lanes.
+__device__ __forceinline__ void batch_slots(const DecodeArgs& a, const Sched& sc, unsigned n0, int b, int lane,
+                                            unsigned& first, unsigned& k) {
+  const unsigned S = (unsigned)(a.Hkv * a.num_rblocks);
+  unsigned cum = 0;
   first = 0;
   k = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int bb = b0 + lane;
-    const int kb = bb < a.B ? num_ranges(key_tiles(a, bb), a.budget, U) : 0;
-    const long cnt = (long)a.Hkv * a.num_rblocks * kb;
-    const long incl = wave_incl_scan(cnt, lane) + cum;
+    const unsigned kb = num_ranges(b0 == 0 ? n0 : chunk_tiles(a, b0, lane), sc.P, sc.U);
+    const unsigned incl = wave_scan(S * kb) + cum;
     const int src = b - b0 < 0 ? 0 : (b - b0 > 63 ? 63 : b - b0);
-    const long excl_src = __shfl(incl - cnt, src, 64);
-    const int k_src = __shfl(kb, src, 64);
+    const unsigned excl_src = (unsigned)__shfl((int)(incl - S * kb), src, 64);
+    const unsigned k_src = (unsigned)__shfl((int)kb, src, 64);
     if (b >= b0 && b < b0 + 64) {
       first = excl_src;
       k = k_src;
     }
-    cum = __shfl(incl, 63, 64);
+    cum = lane_value(incl, 63);
   }
 }
 
@@ -155,28 +168,28 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   const int kk = wave >> 1;  // key block within each tile
 
   // Find this workgroup's range (the same in every wave).
-  const long U = total_tiles(a, lane);
-  if (U == 0) return;
-  const int slot = blockIdx.x;
+  const unsigned n0 = chunk_tiles(a, 0, lane);
+  const Sched sc = schedule(a, n0, lane);
+  if (sc.U == 0) return;
+  const unsigned slot = blockIdx.x;
   int b = -1, n = 0, k = 0, local = 0;
   {
-    long cum = 0;
+    const unsigned S = (unsigned)(a.Hkv * a.num_rblocks);
+    unsigned cum = 0;
     for (int b0 = 0; b0 < a.B; b0 += 64) {
-      const int bb = b0 + lane;
-      const int nb = bb < a.B ? key_tiles(a, bb) : 0;
-      const int kb = num_ranges(nb, a.budget, U);
-      const long cnt = (long)a.Hkv * a.num_rblocks * kb;
-      const long incl = wave_incl_scan(cnt, lane) + cum;
-      const unsigned long long hit = __builtin_amdgcn_ballot_w64((long)slot < incl);
+      const unsigned nb = b0 == 0 ? n0 : chunk_tiles(a, b0, lane);
+      const unsigned kb = num_ranges(nb, sc.P, sc.U);
+      const unsigned incl = wave_scan(S * kb) + cum;
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(slot < incl);
       if (hit != 0) {
         const int L = __builtin_ctzll(hit);
         b = b0 + L;
-        n = __shfl(nb, L, 64);
-        k = __shfl(kb, L, 64);
-        local = (int)(slot - (__shfl(incl, L, 64) - __shfl(cnt, L, 64)));
+        n = (int)lane_value(nb, L);
+        k = (int)lane_value(kb, L);
+        local = (int)(slot - (lane_value(incl, L) - S * (unsigned)k));
         break;
       }
-      cum = __shfl(incl, 63, 64);
+      cum = lane_value(incl, 63);
     }
   }
   if (b < 0) return;
@@ -387,12 +400,16 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(DecodeArgs a) 
 
   // First slot and number of ranges of this row's segment (same schedule as
   // the split kernel).
-  const long U = total_tiles(a, threadIdx.x & 63);
+  const int lane = threadIdx.x & 63;
+  const unsigned n0 = chunk_tiles(a, 0, lane);
+  const Sched sc = schedule(a, n0, lane);
   long first = 0;
   int k = 0;
-  if (U > 0) {
-    batch_slots(a, U, b, threadIdx.x & 63, first, k);
-    first += (long)(kh * a.num_rblocks + rbi) * k;
+  if (sc.U > 0) {
+    unsigned f = 0, kk = 0;
+    batch_slots(a, sc, n0, b, lane, f, kk);
+    k = (int)kk;
+    first = (long)f + (long)(kh * a.num_rblocks + rbi) * k;
   }
   if (!row_ok) return;
 

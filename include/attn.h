@@ -192,7 +192,9 @@ size_t attn_decode_workspace_size(const attn_params_t* p, int32_t num_splits);
  * past kv_lens[b] are never read. kv_lens = valid length per batch (NULL =
  * Tkv). o [B,Tq,Hq,D] bf16; lse fp32 [B,Hq,Tq] or NULL. A row with no valid
  * key gets O = 0 and LSE = -inf. num_splits < 0 -> ATTN_ERR_INVALID; a
- * workspace smaller than attn_decode_workspace_size -> ATTN_ERR_WORKSPACE. */
+ * workspace smaller than attn_decode_workspace_size -> ATTN_ERR_WORKSPACE;
+ * B * Hkv * ceil(Tq * Hq / Hkv / 64) * ceil(Tkv / 64) >= 2^31 (the kernels
+ * count key tiles in 32 bits) -> ATTN_ERR_UNSUPPORTED. */
 attn_status_t attn_decode(const attn_params_t* p, const void* q, const void* k_cache, const void* v_cache,
                           void* o, float* lse, int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);

@@ -149,6 +149,13 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert L.attn_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, -1, FAKE, wneed, None) == attn.ATTN_ERR_INVALID
     dc = P(Tq=16, Tkv=16384, Hq=32, Hkv=8, causal=False, dtype=attn.ATTN_FP32)
     assert L.attn_decode(ctypes.byref(dc), FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, wneed, None) == attn.ATTN_ERR_UNSUPPORTED
+    # The decode kernels count key tiles of all segments in 32 bits: 2^14
+    # segments (2^20 queries in 64-row blocks) of 2^17 key tiles each are
+    # refused before any launch.
+    dbig = P(B=1, Tq=1 << 20, Tkv=1 << 23, Hq=1, Hkv=1)
+    assert L.attn_decode(ctypes.byref(dbig), FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 1 << 40, None) == \
+        attn.ATTN_ERR_UNSUPPORTED
+    assert b"2^31" in L.attn_last_error()
 
 
 def test_status_strings():

@@ -145,3 +145,63 @@ def test_decode_workspace_reuse():
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
         assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_decode_one_workspace_over_new_inputs_and_many_calls():
+    """With one workspace, calls on new inputs of the same shape each match
+    the oracle (a combine that read a previous call's partials would not), and
+    twenty calls on the same inputs give the same bits."""
+    import torch
+    from forward_backward_amd import attn
+    case = SMALL[1]
+    ws = None
+    for seed in (0, 1, 2):
+        host, dev, f64 = device_inputs(case, seed=seed, with_do=False)
+        if ws is None:
+            ws = attn.decode_workspace(dev["q"], dev["k"])
+        print(f"[decode new inputs] {case.name} seed={seed}", flush=True)
+        o, lse = attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=case.scale, workspace=ws)
+        torch.cuda.synchronize()
+        ro, rlse = oracle.attention_decode(f64["q"], f64["k"], f64["v"], case.scale, f64["kv_lens"])
+        assert rel_err(to_host64(o), ro) <= TOL["bf16"]
+        check_lse(to_host64(lse), rlse)
+    (big,) = workload_cases(4)
+    _, dev, _ = device_inputs(big, with_do=False)
+    ws = attn.decode_workspace(dev["q"], dev["k"])
+    ref = attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=big.scale, workspace=ws)
+    for it in range(20):
+        o, lse = attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=big.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16)), f"call {it}"
+        assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32)), f"call {it}"
+
+
+def test_decode_graph_replays():
+    """Each replay of a captured decode call (with eager calls on the same
+    workspace in between) equals the eager result bit for bit."""
+    import torch
+    from forward_backward_amd import attn
+    (case,) = workload_cases(4)
+    _, dev, _ = device_inputs(case, with_do=False)
+    ws = attn.decode_workspace(dev["q"], dev["k"])
+    ref = attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=case.scale, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        out = attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        print(f"[decode graph] replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[0].view(torch.int16), ref[0].view(torch.int16)), f"replay {rep}"
+        assert torch.equal(out[1].view(torch.int32), ref[1].view(torch.int32)), f"replay {rep}"
+        eager = attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=case.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(eager[0].view(torch.int16), ref[0].view(torch.int16))
