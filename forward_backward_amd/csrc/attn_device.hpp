@@ -202,19 +202,35 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // M0 is saved and restored around the copy (the compiler neither knows nor
 // expects it to change); the LDS address must be wave-uniform and is moved
 // into a scalar register first.
+//
+// NT = true marks the copy non-temporal (the nt cache policy): for data read
+// exactly once, such as a decode's KV cache, which then does not compete for
+// the L2 with other streams.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   ATTN_DBG_CHECK(g, 16);
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(base)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(base)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(base)
+        : "memory");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   ATTN_DBG_CHECK(g, 4);
@@ -278,7 +294,7 @@ __host__ __device__ __forceinline__ uint64_t join_halves(uint32_t lo, uint32_t h
 // VISIBLE = true issues the copy through the compiler builtin instead, so the
 // compiler orders later LDS reads after it itself (it cannot tell stages of
 // one array apart and waits before transpose reads in particular).
-template <int D, int ROWS, int THREADS, bool VISIBLE = false>
+template <int D, int ROWS, int THREADS, bool VISIBLE = false, bool NT = false>
 __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long rs, int r0, int rlim, int tid) {
   using Gm = TileGeom<D, ROWS, THREADS>;
   const int lane = tid & 63, wave = tid >> 6;
@@ -292,7 +308,7 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)dst, 16, 0, 0);
     }
     else
-      dma16(src, lds_addr(dst));
+      dma16<NT>(src, lds_addr(dst));
   }
 }
 
@@ -302,6 +318,7 @@ __device__ __forceinline__ void dma_tile(uint16_t* tile, const uint16_t* g, long
 // readfirstlane) so that it always lands in scalar registers. readfirstlane
 // returns a signed int: each half is taken back as uint32_t before widening,
 // or a low half with bit 31 set would sign-extend over the high half.
+template <bool NT = false>
 __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
@@ -309,15 +326,26 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
   const void* sbase = reinterpret_cast<const void*>(join_halves(lo, hi));
   ATTN_DBG_CHECK(static_cast<const char*>(sbase) + voff, 16);
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
 }
 
 // Batched dma16_s: the ITERS copies of one tile (lane byte offsets voff[i],
@@ -325,18 +353,21 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
 // of a second tile from base_b to lds + AB + i * STEP, in one inline-asm
 // block, so that M0 is saved and restored once per batch and each further
 // destination is one scalar add of an immediate. lds must be wave-uniform.
-#define ATTN_DMA_AT(v, b) "s_nop 0\n\tglobal_load_lds_dwordx4 %[" v "], %[" b "]\n\t"
+#define ATTN_DMA_AT(v, b) "s_nop 0\n\tglobal_load_lds_dwordx4 %[" v "], %[" b "]" ATTN_DMA_POL "\n\t"
 #define ATTN_DMA_STEP(d) "s_add_u32 m0, m0, %[" d "]\n\t"
+#define ATTN_DMA_POL ""
+#define ATTN_DMA_NT false
+#define DMA16_BATCH_NAME dma16_batch_plain
 template <int ITERS, int STEP, bool TWO, int AB = 0>
-__device__ __forceinline__ void dma16_batch(const void* base_a, const void* base_b, const uint32_t (&voff)[ITERS],
+__device__ __forceinline__ void DMA16_BATCH_NAME(const void* base_a, const void* base_b, const uint32_t (&voff)[ITERS],
                                             uint32_t lds) {
   if constexpr (ITERS != 2 && ITERS != 4) {
     // Other counts (head_dim 32 and 256 tiles of some kernels): one copy at a time.
 #pragma unroll
-    for (int i = 0; i < ITERS; ++i) dma16_s(base_a, voff[i], lds + i * STEP);
+    for (int i = 0; i < ITERS; ++i) dma16_s<ATTN_DMA_NT>(base_a, voff[i], lds + i * STEP);
     if constexpr (TWO) {
 #pragma unroll
-      for (int i = 0; i < ITERS; ++i) dma16_s(base_b, voff[i], lds + AB + i * STEP);
+      for (int i = 0; i < ITERS; ++i) dma16_s<ATTN_DMA_NT>(base_b, voff[i], lds + AB + i * STEP);
     }
     return;
   }
@@ -392,6 +423,89 @@ __device__ __forceinline__ void dma16_batch(const void* base_a, const void* base
                  : "memory");
   }
 }
+#undef DMA16_BATCH_NAME
+#undef ATTN_DMA_NT
+#undef ATTN_DMA_POL
+#define ATTN_DMA_POL " nt"
+#define ATTN_DMA_NT true
+#define DMA16_BATCH_NAME dma16_batch_nt
+template <int ITERS, int STEP, bool TWO, int AB = 0>
+__device__ __forceinline__ void DMA16_BATCH_NAME(const void* base_a, const void* base_b, const uint32_t (&voff)[ITERS],
+                                            uint32_t lds) {
+  if constexpr (ITERS != 2 && ITERS != 4) {
+    // Other counts (head_dim 32 and 256 tiles of some kernels): one copy at a time.
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) dma16_s<ATTN_DMA_NT>(base_a, voff[i], lds + i * STEP);
+    if constexpr (TWO) {
+#pragma unroll
+      for (int i = 0; i < ITERS; ++i) dma16_s<ATTN_DMA_NT>(base_b, voff[i], lds + AB + i * STEP);
+    }
+    return;
+  }
+  auto uniform = [](const void* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32)));
+    return reinterpret_cast<const void*>(join_halves(lo, hi));
+  };
+  const void* sa = uniform(base_a);
+#ifdef ATTN_DEBUG
+#pragma unroll
+  for (int i = 0; i < ITERS; ++i) {
+    ATTN_DBG_CHECK(static_cast<const char*>(sa) + voff[i], 16);
+    if constexpr (TWO) ATTN_DBG_CHECK(static_cast<const char*>(uniform(base_b)) + voff[i], 16);
+  }
+#endif
+  const uint32_t l0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+  uint32_t saved;
+  if constexpr (ITERS == 2 && !TWO) {
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [a] "s"(sa), [l0] "s"(l0), [st] "n"(STEP)
+                 : "memory");
+  } else if constexpr (ITERS == 2 && TWO) {
+    const void* sb = uniform(base_b);
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") ATTN_DMA_STEP("ab") ATTN_DMA_AT("v0", "b") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "b") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [a] "s"(sa), [b] "s"(sb), [l0] "s"(l0), [st] "n"(STEP),
+                   [ab] "n"(AB - STEP)
+                 : "memory");
+  } else if constexpr (ITERS == 4 && !TWO) {
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") ATTN_DMA_STEP("st") ATTN_DMA_AT("v2", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v3", "a") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]), [a] "s"(sa),
+                   [l0] "s"(l0), [st] "n"(STEP)
+                 : "memory");
+  } else if constexpr (ITERS == 4 && TWO) {
+    const void* sb = uniform(base_b);
+    asm volatile("s_mov_b32 %[sv], m0\n\ts_mov_b32 m0, %[l0]\n\t" ATTN_DMA_AT("v0", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "a") ATTN_DMA_STEP("st") ATTN_DMA_AT("v2", "a") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v3", "a") ATTN_DMA_STEP("ab") ATTN_DMA_AT("v0", "b") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v1", "b") ATTN_DMA_STEP("st") ATTN_DMA_AT("v2", "b") ATTN_DMA_STEP("st")
+                 ATTN_DMA_AT("v3", "b") "s_mov_b32 m0, %[sv]"
+                 : [sv] "=&s"(saved)
+                 : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]), [a] "s"(sa),
+                   [b] "s"(sb), [l0] "s"(l0), [st] "n"(STEP), [ab] "n"(AB - 3 * STEP)
+                 : "memory");
+  }
+}
+#undef DMA16_BATCH_NAME
+#undef ATTN_DMA_NT
+#undef ATTN_DMA_POL
+// The batch with the default cache policy, or (NT) non-temporal as for dma16.
+template <int ITERS, int STEP, bool TWO, int AB = 0, bool NT = false>
+__device__ __forceinline__ void dma16_batch(const void* base_a, const void* base_b, const uint32_t (&voff)[ITERS],
+                                            uint32_t lds) {
+  if constexpr (NT)
+    dma16_batch_nt<ITERS, STEP, TWO, AB>(base_a, base_b, voff, lds);
+  else
+    dma16_batch_plain<ITERS, STEP, TWO, AB>(base_a, base_b, voff, lds);
+}
 #undef ATTN_DMA_AT
 #undef ATTN_DMA_STEP
 
@@ -426,11 +540,11 @@ struct TileCopy {
 
   // Rows [r0, r0 + ROWS) of two matrices with the same row stride into two
   // tiles `ab_bytes` apart in LDS (tile_b = tile_a + AB bytes), one batch.
-  template <int AB>
+  template <int AB, bool NT = false>
   __device__ __forceinline__ void copy2(uint16_t* tile_a, const uint16_t* ga, const uint16_t* gb, long rs,
                                         int r0) const {
     const long off = (long)r0 * rs;
-    dma16_batch<ITERS, WAVES * 1024, true, AB>(ga + off, gb + off, voff, lds_addr(tile_a) + lds_wave);
+    dma16_batch<ITERS, WAVES * 1024, true, AB, NT>(ga + off, gb + off, voff, lds_addr(tile_a) + lds_wave);
   }
   // One tile, one batch.
   __device__ __forceinline__ void copy1(uint16_t* tile, const uint16_t* g, long rs, int r0) const {
