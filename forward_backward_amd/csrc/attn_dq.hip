@@ -306,7 +306,9 @@ template <int D>
 __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
   using C = DqPairCfg<D>;
   __shared__ __attribute__((aligned(16))) uint16_t tiles[2 * C::NST * C::TILE];  // stage s: K at 2s, V at 2s + 1
+  __shared__ __attribute__((aligned(16))) uint16_t rows_x[2 * C::BM * D];         // the tile's dO rows, then O rows
   static_assert(2 * C::NST * C::TILE * 2 >= 4 * 64 * 16 * C::DB * 4, "the partial hand-over reuses the tiles");
+  static_assert(C::NST >= 3 && 2 * C::TILE == C::BM * D, "the tile's Q rows fill ring stage 2");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -338,15 +340,73 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
   const int j0 = kv_first / C::BN;
   const int ntiles = kv_end > kv_first ? (kv_end + C::BN - 1) / C::BN - j0 : 0;
 
+  // Copies of tile `it` into stage `st`. They go through inline assembly, which
+  // the compiler does not see writing LDS: the waits before each step's
+  // barrier order them (CP copy instructions per wave and tile, full or partial).
+  const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
+  [[maybe_unused]] constexpr int CP = 2 * TileCopy<D, C::BN, C::THREADS>::ITERS;
+  auto issue = [&](int it, int st) {
+    uint16_t* ks = tiles + st * 2 * C::TILE;
+    const int k0 = (j0 + it) * C::BN;
+    if (k0 + C::BN <= kv_end) {
+      // One copy at a time here: one batch for both tiles measured 1% slower.
+      kvcopy.copy(ks, kb, krs, k0);
+      kvcopy.copy(ks + C::TILE, vb, krs, k0);
+    } else {
+      dma_tile<D, C::BN, C::THREADS>(ks, kb, krs, k0, kv_end, tid);
+      dma_tile<D, C::BN, C::THREADS>(ks + C::TILE, vb, krs, k0, kv_end, tid);
+    }
+  };
+
+  // The tile's Q, dO and O rows stream into LDS together with the first two
+  // K/V tiles, so that the start of a tile costs one memory round trip: Q into
+  // ring stage 2 (refilled only after the loop's first barrier), dO and O into
+  // rows_x, by the same coalesced 1 KiB copies in the swizzled tile layout as
+  // the K/V tiles. (Loaded straight into registers, each 16-byte fragment load
+  // touched 32 rows per instruction, and the rows took about 9 us per tile to
+  // arrive under load.) Rows past Tq re-read the last row; their lanes are
+  // zeroed below.
+  uint16_t* const q_lds = tiles + 2 * 2 * C::TILE;
+  {
+    const TileCopy<D, C::BM, C::THREADS> rcopy(qrs, tid);
+    auto rows = [&](uint16_t* dst, const void* src) {
+      const uint16_t* g = (const uint16_t*)src + qoff;
+      if (q0 + C::BM <= a.Tq)
+        rcopy.copy1(dst, g, qrs, q0);
+      else
+        dma_tile<D, C::BM, C::THREADS>(dst, g, qrs, q0, a.Tq, tid);
+    };
+    rows(q_lds, a.q);
+    rows(rows_x, a.dout);
+    if (a.dq_stats) rows(rows_x + C::BM * D, a.o);
+  }
+  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+
   const int qrow = q0 + 32 * w4 + l32;
   const bool row_ok = qrow < a.Tq;
+  const long stat = ((long)b * a.Hq + h) * a.Tq + qrow;
+  // The rows' statistics (compiler-visible loads, issued after the copies: the
+  // wait for them below is a wait for everything, rows and first tiles alike).
+  float lse_in = 0.f, lse2_in = INFINITY, dlt_in = 0.f;
+  if (row_ok) {
+    if (a.dq_stats) {
+      lse_in = a.lse[stat];
+    } else {
+      lse2_in = a.lse2[stat];
+      dlt_in = a.delta[stat];
+    }
+  }
+  wait_vmem();
+  __syncthreads();
   u32x4_t qf[C::KS], gf[C::KS];
+  const int lrow = 32 * w4 + l32;  // the lane's row in the tile
 #pragma unroll
   for (int t = 0; t < C::KS; ++t) {
-    qf[t] = row_ok ? gload16((const uint16_t*)a.q + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
-    gf[t] = row_ok ? gload16((const uint16_t*)a.dout + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+    const int off = swz_off<D>(lrow, 16 * t + 8 * hh);
+    qf[t] = row_ok ? lds_read16(q_lds + off) : u32x4_t{0, 0, 0, 0};
+    gf[t] = row_ok ? lds_read16(rows_x + off) : u32x4_t{0, 0, 0, 0};
   }
-  const long stat = ((long)b * a.Hq + h) * a.Tq + qrow;
   float lse2, dlt;
   if (a.dq_stats) {
     // D of the lane's row from its O and dO fragments (the pre-kernel's
@@ -355,16 +415,16 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     u32x4_t of[C::KS];
 #pragma unroll
     for (int t = 0; t < C::KS; ++t)
-      of[t] = row_ok ? gload16((const uint16_t*)a.o + qoff + qrow * qrs + 16 * t + 8 * hh) : u32x4_t{0, 0, 0, 0};
+      of[t] = row_ok ? lds_read16(rows_x + C::BM * D + swz_off<D>(lrow, 16 * t + 8 * hh)) : u32x4_t{0, 0, 0, 0};
     const float dsum = half_sum(row_dot_half<C::KS>(of, gf));
-    const float lse = row_ok ? a.lse[stat] : 0.f;
+    const float lse = lse_in;
     if (row_ok && half == 0 && hh == 0) write_row_stats(a, stat, dsum, lse);
     lse2 = row_ok ? lse * 1.4426950408889634f : INFINITY;
     dlt = row_ok ? dsum : 0.f;
     if (blockIdx.x == 0 && tid < kBwdQueueWords && a.queue != nullptr) a.queue[tid] = 0u;
   } else {
-    lse2 = row_ok ? a.lse2[stat] : INFINITY;
-    dlt = row_ok ? a.delta[stat] : 0.f;
+    lse2 = lse2_in;
+    dlt = dlt_in;
   }
   const float c = a.scale_log2;
 
@@ -388,24 +448,6 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     trd[db][0] = swz_off<D>(tr_row, 32 * db + tr_col) + 32 * half * D;
     trd[db][1] = swz_off<D>(tr_row + 8, 32 * db + tr_col) + 32 * half * D;
   }
-
-  // Copies of tile `it` into stage `st`. They go through inline assembly, which
-  // the compiler does not see writing LDS: the waits before each step's
-  // barrier order them (CP copy instructions per wave and tile, full or partial).
-  const TileCopy<D, C::BN, C::THREADS> kvcopy(krs, tid);
-  [[maybe_unused]] constexpr int CP = 2 * TileCopy<D, C::BN, C::THREADS>::ITERS;
-  auto issue = [&](int it, int st) {
-    uint16_t* ks = tiles + st * 2 * C::TILE;
-    const int k0 = (j0 + it) * C::BN;
-    if (k0 + C::BN <= kv_end) {
-      // One copy at a time here: one batch for both tiles measured 1% slower.
-      kvcopy.copy(ks, kb, krs, k0);
-      kvcopy.copy(ks + C::TILE, vb, krs, k0);
-    } else {
-      dma_tile<D, C::BN, C::THREADS>(ks, kb, krs, k0, kv_end, tid);
-      dma_tile<D, C::BN, C::THREADS>(ks + C::TILE, vb, krs, k0, kv_end, tid);
-    }
-  };
 
   // One 32-key block: S^T, dP^T, the masked dS^T, then dQ^T += K^T dS^T. The
   // element-wise mask is a select-only fix-up under a uniform branch (a
@@ -478,12 +520,7 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
     // Two tiles per step and one barrier: tile t sits in stage t % 4; the
     // copies of the next step's two tiles start after the step's barrier, once
     // every wave is done with the two tiles before, and land before its end.
-    if (ntiles > 0) issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
-    // The Q and dO fragments and the first tiles have landed; waiting here also
-    // keeps the compiler, which only sees the fragment loads, from placing its
-    // own wait for them inside the loop.
-    wait_vmem();
+    // The first tiles landed in the prologue.
     for (int it = 0; it < ntiles; it += 2) {
       __syncthreads();  // tiles it, it + 1 visible; tiles it - 2, it - 1 read by every wave
       if (it + 2 < ntiles) issue(it + 2, (it + 2) % C::NST);
@@ -499,12 +536,7 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
       wait_vmem();  // the next step's tiles have landed
     }
   } else {
-    if (ntiles > 0) issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
-    // The Q and dO fragments and the first tiles have landed: without this the
-    // compiler, which only sees the fragment loads, waits for them inside the
-    // loop, where the wait would also drain the copies in flight.
-    wait_vmem();
+    // The first tiles landed in the prologue.
     int st_rd = 0, st_wr = 2;
     for (int it = 0; it < ntiles; ++it) {
       // Tile it has landed once at most the copies of tile it + 1 are in flight.
