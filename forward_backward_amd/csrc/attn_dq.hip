@@ -567,8 +567,11 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
       for (int r = 0; r < 16; ++r) xf[(16 * db + r) * 64 + lane] = acc[db][r];
   }
   __syncthreads();
-  if (half == 0 && row_ok) {
-    uint16_t* dqp = (uint16_t*)a.dq + qoff + qrow * qrs;
+  // The sums go to a bf16 tile in LDS (rows_x, free by now; the swizzled
+  // layout of the copies), and from there to dQ in whole 256-byte rows, 16
+  // bytes per lane: stored straight from the fragments, each instruction would
+  // write 8 bytes to each of 32 rows.
+  if (half == 0) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -580,8 +583,19 @@ __global__ __launch_bounds__(512) void attn_dq_pair_kernel(BwdArgs a) {
           v[x] = (acc[db][r] + xf[(16 * db + r) * 64 + lane]) * a.scale;
         }
         const int d = 32 * db + 8 * g + 4 * hh;
-        *(u32x2_t*)(dqp + d) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        *(u32x2_t*)(rows_x + swz_off<D>(lrow, d)) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
       }
+  }
+  __syncthreads();
+  {
+    using Gm = TileGeom<D, C::BM, C::THREADS>;
+    uint16_t* const dqb = (uint16_t*)a.dq + qoff;
+#pragma unroll
+    for (int i = 0; i < Gm::ITERS; ++i) {
+      const int r = Gm::row(i, wave, lane);
+      if (q0 + r < a.Tq)
+        *(u32x4_t*)(dqb + Gm::elem(q0 + r, r, lane, qrs)) = lds_read16(rows_x + Gm::block(i, wave) * 512 + lane * 8);
+    }
   }
 }
 
