@@ -53,7 +53,13 @@ struct FwdCfg {
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_s0[C::TILE], k_s1[C::TILE], v_s0[C::TILE], v_s1[C::TILE];
+  // K and V stages; after the tile loop the first two hold the O tile on its way out.
+  __shared__ __attribute__((aligned(16))) uint16_t kv_s[4 * C::TILE];
+  uint16_t* const k_s0 = kv_s;
+  uint16_t* const k_s1 = kv_s + C::TILE;
+  uint16_t* const v_s0 = kv_s + 2 * C::TILE;
+  uint16_t* const v_s1 = kv_s + 3 * C::TILE;
+  static_assert(2 * C::TILE == C::BM * D, "the O tile fills the two K stages");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -285,21 +291,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   const float ltot = half_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (row_ok) {
-    uint16_t* ob = (uint16_t*)a.o + ((long)b * a.Tq * a.Hq + h) * D + qrow * qrs;
+  // O goes to a bf16 tile in LDS (the K stages, whose last reads every wave
+  // has passed: the loop ends on a barrier; the swizzled layout of the
+  // copies) and from there to memory in whole rows, 16 bytes per lane, rather
+  // than 8 bytes to each of 32 rows per instruction.
+  const int lrow = 32 * wave + l32;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * db + 8 * g + 4 * hh;
-        const u32x2_t w = u32x2_t{pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                                  pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        *(u32x2_t*)(ob + d) = w;
-      }
-    if (hh == 0) {
-      const float lse = ltot > 0.f ? m * a.scale + __logf(ltot) : -INFINITY;
-      a.lse[((long)b * a.Hq + h) * a.Tq + qrow] = lse;
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * hh;
+      const u32x2_t w = u32x2_t{pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+      *(u32x2_t*)(kv_s + swz_off<D>(lrow, d)) = w;
     }
+  if (row_ok && hh == 0) {
+    const float lse = ltot > 0.f ? m * a.scale + __logf(ltot) : -INFINITY;
+    a.lse[((long)b * a.Hq + h) * a.Tq + qrow] = lse;
+  }
+  __syncthreads();
+  using Gm = TileGeom<D, C::BM, C::THREADS>;
+  uint16_t* const obase = (uint16_t*)a.o + ((long)b * a.Tq * a.Hq + h) * D;
+#pragma unroll
+  for (int i = 0; i < Gm::ITERS; ++i) {
+    const int r = Gm::row(i, wave, lane);
+    if (q0 + r < a.Tq)
+      *(u32x4_t*)(obase + Gm::elem(q0 + r, r, lane, qrs)) = lds_read16(kv_s + Gm::block(i, wave) * 512 + lane * 8);
   }
 }
 
