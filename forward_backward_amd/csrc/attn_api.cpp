@@ -460,6 +460,7 @@ attn_status_t decode_run(const attn_params_t* p, const void* q, const void* k_ca
   a.budget = num_splits;
   a.num_rblocks = (int)decode_row_blocks(p);
   a.num_slots = (int)(num_splits + segs);
+  a.direct = num_splits == 1;
   const Sizes n = sizes_of(p);
   const attn_status_t st =
       dbg_prepare({{q, n.q * size_t{2}}, {k_cache, n.kv * size_t{2}}, {v_cache, n.kv * size_t{2}}, {o, n.q * size_t{2}},

@@ -30,7 +30,9 @@
 // Combine kernel: for each output row the ranges of its segment are merged
 // in ascending order with a running maximum: LSE = log sum_r exp(LSE_r),
 // O = sum_r exp(LSE_r - LSE) O_r. A row with no valid key gets O = 0 and
-// LSE = -inf.
+// LSE = -inf. With a split budget of 1 every segment is one range: the split
+// kernel then writes O (bf16) and the LSE itself, the bits the combine would
+// make of a single range, and no combine is launched.
 #include <mutex>
 
 #include "../../include/attn.h"
@@ -154,6 +156,47 @@ __device__ __forceinline__ void batch_slots(const DecodeArgs& a, const Sched& sc
   }
 }
 
+// With one range per segment (split budget 1) the split kernel writes the
+// output itself, and the workgroups past the ranges write the rows of the
+// segments without keys: workgroup `e` past the last range takes the e-th such
+// segment (counting batches with no valid key in order, then their segments)
+// and writes O = 0 and LSE = -inf for its rows. A grid of 1 + segments
+// workgroups leaves one for every segment.
+template <int D>
+__device__ __forceinline__ void zero_empty_segment(const DecodeArgs& a, unsigned e, unsigned n0, int lane, int tid) {
+  const unsigned S = (unsigned)(a.Hkv * a.num_rblocks);
+  unsigned cum = 0, local = 0;
+  int b = -1;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const unsigned nb = b0 == 0 ? n0 : chunk_tiles(a, b0, lane);
+    const unsigned cnt = (b0 + lane < a.B && nb == 0) ? S : 0u;
+    const unsigned incl = wave_scan(cnt) + cum;
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(e < incl);
+    if (hit != 0) {
+      const int L = __builtin_ctzll(hit);
+      b = b0 + L;
+      local = e - (lane_value(incl, L) - S);
+      break;
+    }
+    cum = lane_value(incl, 63);
+  }
+  if (b < 0) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  local = __builtin_amdgcn_readfirstlane(local);
+  const int kh = (int)local / a.num_rblocks;
+  const int rbi = (int)local % a.num_rblocks;
+  const int G = a.Hq / a.Hkv;
+  const int R = a.Tq * G;
+  const int p0 = rbi * kDecodeRows;
+  const int np = R - p0 < kDecodeRows ? R - p0 : kDecodeRows;
+  for (int idx = tid; idx < np * (D / 4); idx += 256) {
+    const int p = p0 + idx / (D / 4), part = idx % (D / 4);
+    const int i = p / G, h = kh * G + p % G;
+    *(u32x2_t*)((uint16_t*)a.o + (((long)b * a.Tq + i) * a.Hq + h) * D + 4 * part) = u32x2_t{0u, 0u};
+    if (a.lse != nullptr && part == 0) a.lse[((long)b * a.Hq + h) * a.Tq + i] = -INFINITY;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   using C = DecCfg<D>;
@@ -170,7 +213,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
   // Find this workgroup's range (the same in every wave).
   const unsigned n0 = chunk_tiles(a, 0, lane);
   const Sched sc = schedule(a, n0, lane);
-  if (sc.U == 0) return;
+  if (sc.U == 0 && !a.direct) return;
   const unsigned slot = blockIdx.x;
   int b = -1, n = 0, k = 0, local = 0;
   {
@@ -191,8 +234,12 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
       }
       cum = lane_value(incl, 63);
     }
+    if (b < 0) {
+      // Past the last range (cum ranges in all).
+      if (a.direct) zero_empty_segment<D>(a, slot - cum, n0, lane, tid);
+      return;
+    }
   }
-  if (b < 0) return;
   b = __builtin_amdgcn_readfirstlane(b);
   n = __builtin_amdgcn_readfirstlane(n);
   k = __builtin_amdgcn_readfirstlane(k);
@@ -361,7 +408,26 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(DecodeArgs a) {
     const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2((m1 - mref) * c);
     const float ltot = half_sum(lsum * a0 + l1 * a1);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (row_ok) {
+    if (row_ok && a.direct) {
+      // The segment's only range: its normalised partial is the output (the
+      // combine would weight it by 1 and divide by 1), bf16, and its LSE.
+      const int i = prow / G, h = kh * G + prow % G;
+      uint16_t* op = (uint16_t*)a.o + (((long)b * a.Tq + i) * a.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float w[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = 4 * g + x;
+            w[x] = (o[db][r] * a0 + mg[(16 * db + r) * 64 + lane] * a1) * inv;
+          }
+          *(u32x2_t*)(op + 32 * db + 8 * g + 4 * hh) = u32x2_t{pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3])};
+        }
+      if (hh == 0 && a.lse != nullptr)
+        a.lse[((long)b * a.Hq + h) * a.Tq + i] = ltot > 0.f ? mt * a.scale + __logf(ltot) : -INFINITY;
+    } else if (row_ok) {
       const long prt = (long)slot * C::ROWS + 32 * rb + l32;
       float* po = a.part_o + prt * D;
 #pragma unroll
@@ -461,6 +527,10 @@ void launch_decode(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const long R = (long)a.Tq * G;
   if (R == 0 || a.B == 0) return;
+  if (a.direct) {
+    hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3((unsigned)a.num_slots), dim3(256), 0, st, a);
+    return;
+  }
   if (a.Tkv > 0)
     hipLaunchKernelGGL(attn_decode_split_kernel<D>, dim3((unsigned)a.num_slots), dim3(256), 0, st, a);
   const long threads = (long)a.B * a.Hkv * R * (D / 4);

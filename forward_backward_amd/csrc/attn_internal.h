@@ -69,6 +69,7 @@ struct DecodeArgs {
   int budget;              // P: key ranges are sized as if P workgroups shared all key tiles
   int num_rblocks;         // packed row blocks per (batch, KV head)
   int num_slots;           // P + B * Hkv * num_rblocks (upper bound on the key ranges)
+  int direct;              // P == 1: one range per segment, written as the output itself (no combine)
 };
 
 // Launchers (each returns the hipGetLastError() after its launches).

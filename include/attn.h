@@ -186,7 +186,10 @@ size_t attn_decode_workspace_size(const attn_params_t* p, int32_t num_splits);
  * with n tiles is cut into min(n, ceil(n * P / U)) near-equal key ranges, so
  * no range exceeds ceil(U / P) tiles. The schedule is computed on the device
  * from kv_lens; results depend on it only through rounding and are bitwise
- * reproducible for the same inputs and budget.
+ * reproducible for the same inputs and budget. With a budget of 1 (the
+ * automatic budget once B * Hkv * ceil(Tq * Hq / Hkv / 64) reaches 255) every
+ * segment is one range and the split kernel writes O and the LSE itself,
+ * without the combine (the same bits the combine makes of one range).
  * Non-causal (p->causal must be 0); bf16 only.
  * q [B,Tq,Hq,D]; k_cache/v_cache [B,Tkv,Hkv,D] (Tkv = capacity); keys at or
  * past kv_lens[b] are never read. kv_lens = valid length per batch (NULL =

@@ -205,3 +205,40 @@ def test_decode_graph_replays():
         eager = attn.decode(dev["q"], dev["k"], dev["v"], kv_lens=dev["kv_lens"], scale=case.scale, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(eager[0].view(torch.int16), ref[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("case,splits", [
+    # 256 segments (64 batches x 4 KV heads, one row block): the automatic
+    # split budget is 1, so the kernel writes the output itself; a quarter of
+    # the batches have no valid key and get their rows from spare workgroups.
+    (Case("dec_direct_b64_seg256", 64, 1, 1000, 16, 4, 128, kv_lens=tuple((0, 1, 640, 999)[b % 4] for b in range(64)),
+          workload_id=220, decode=True), 0),
+    (Case("dec_direct_d64_empty_batch", 2, 5, 2048, 16, 2, 64, kv_lens=(0, 2048), workload_id=203, decode=True), 1),
+    (Case("dec_direct_empty_cache", 2, 3, 0, 4, 1, 64, workload_id=211, decode=True), 1),
+], ids=lambda x: x.name if hasattr(x, "name") else f"splits{x}")
+def test_decode_one_range_per_segment_writes_the_output(case, splits):
+    """With a split budget of 1 every segment is one key range and the split
+    kernel writes O and the LSE itself (no combine launch); rows of segments
+    without keys come from the workgroups past the last range. Checked against
+    the oracle, zero rows, and bit-for-bit reruns."""
+    import torch
+    from forward_backward_amd import attn
+    if splits == 0:
+        assert attn.decode_num_splits(case.B, case.Tq, case.Tkv, case.Hq, case.Hkv, case.D) == 1
+    host, dev, f64 = device_inputs(case, with_do=False)
+    print(f"[decode direct] {case.name} splits={splits}", flush=True)
+    o, lse = run_decode(case, dev, splits)
+    o2, lse2 = run_decode(case, dev, splits)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    go, glse = to_host64(o), to_host64(lse)
+    lens = host["kv_lens"] if host["kv_lens"] is not None else np.full(case.B, case.Tkv)
+    for b in range(case.B):
+        if min(max(int(lens[b]), 0), case.Tkv) == 0:
+            assert np.all(go[b] == 0.0) and np.all(np.isneginf(glse[b])), f"batch {b}"
+    if case.Tkv == 0:
+        return
+    ro, rlse = oracle.attention_decode(f64["q"], f64["k"], f64["v"], case.scale, f64["kv_lens"])
+    err = rel_err(go, ro)
+    assert err <= TOL["bf16"], f"{case.name}: O rel err {err:.3e}"
+    check_lse(glse, rlse)
