@@ -1,8 +1,8 @@
 """CPU float64 oracle for fused exact attention (test infrastructure only).
 
 This package is the reference the tests compare against, not the product.
-Only the test suite, the smoke check in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may
-import it. It shares no code with the HIP library in ``forward_backward_amd``
+Only the test suite, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. It shares no code with the HIP library in ``forward_backward_amd``
 and imports nothing from it.
 
 Every function is the plain dense definition of scaled-dot-product attention
